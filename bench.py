@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE layer step (forward + backward) on one MI355X.
+
+A step runs every stage of the path on one batch of synthetic input already
+resident in HBM: route, dispatch (with the EP send layout), grouped expert
+FFN forward (routed, then shared experts), combine, combine backward, grouped
+expert FFN backward, router backward, dispatch backward.
+
+Prints ONE JSON line (stdout):
+  value       tokens per second of the whole step (T / step time)
+  roofline    the grouped expert GEMM (all its launches in a step): algorithmic
+              FLOPs (3 x 2 n d F m, plus shared experts) / its event-measured
+              time, against the bf16 dense MFMA peak
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+  kernels     per-entry-point times and achieved rates (events around each call)
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, n, T_kept):
+    """Algorithmic bytes / FLOPs of each entry point for one step."""
+    s = 2 if wl.dtype == "bf16" else 4
+    T, d, F, E, k = wl.T, wl.d, wl.ffn, wl.E, wl.k
+    m = 3 if wl.act == "swiglu" else 2
+    Fs = wl.n_shared * wl.ffn_shared
+    out = {}
+    out["route"] = dict(bytes=T * d * s + d * E * s + T * E * 4 + 8 * T * k)
+    out["dispatch"] = dict(bytes=T_kept * d * s + n * d * s + 8 * T * k + 4 * n)
+    out["ffn_fwd"] = dict(flops=2 * n * d * F * m)
+    out["combine"] = dict(bytes=n * d * s + T * d * s + (T * d * s if Fs else 0) + 8 * T * k)
+    out["combine_bwd"] = dict(bytes=T * d * s + 2 * n * d * s + 12 * T * k)
+    out["ffn_bwd"] = dict(flops=2 * 2 * n * d * F * m)
+    out["route_bwd"] = dict(bytes=T * d * s + T * E * 4 * 2 + d * E * s + T * k * 8)
+    out["dispatch_bwd"] = dict(bytes=n * d * s + T * d * s + (T * d * s if Fs else 0) + T * E * 4 + 4 * T * k
+                               + d * E * s)
+    if Fs:
+        out["shared_fwd"] = dict(flops=2 * T * d * Fs * m)
+        out["shared_bwd"] = dict(flops=2 * 2 * T * d * Fs * m)
+    return out
+
+
+def cpu_baseline(wl, inp, n_tokens):
+    """Time the oracle (float64 numpy) on the first n_tokens tokens of the
+    workload with its full weights, with all host cores available to BLAS."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    t_s = min(n_tokens, wl.T)
+    f = oracle.to_f64
+    X, DY = f(inp.x[:t_s]), f(inp.dy[:t_s])
+    wr, b = f(inp.w_router), (None if inp.bias is None else f(inp.bias))
+    w1, wu, w2 = f(inp.w1), f(inp.w_up), f(inp.w2)
+    sg, su, sd = f(inp.ws_gate), f(inp.ws_up), f(inp.ws_down)
+    with threadpool_limits(limits=cores):
+        info = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        t0 = time.perf_counter()
+        oracle.layer_forward_backward(X, wr, b, w1, wu, w2, DY, k=wl.k, gating=wl.gating, act=wl.act,
+                                      capacity_factor=wl.capacity_factor, ep_ranks=wl.ep_ranks,
+                                      placement=wl.placement, ws_gate=sg, ws_up=su, ws_down=sd,
+                                      n_shared=wl.n_shared)
+        dt = time.perf_counter() - t0
+    return {"value": round(t_s / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle fwd+bwd on the first {t_s} of {wl.T} tokens of {wl.name} with the "
+                      f"full weights ({dt:.2f} s, {cores} host cores visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
+                                   "it runs on exactly one GPU (--gpus 1)"}))
+        return 2
+
+    import torch
+    import synth
+    from mixture_experts_layer_36_amd import _native
+    from mixture_experts_layer_36_amd.layer import MoELayer, Weights
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    _native.load()
+    wl = synth.workload(args.workload)
+    log(f"[bench] workload {wl.name}: generating inputs")
+    inp = synth.make_inputs(wl)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    layer = MoELayer(wl.T, wl.d, wl.ffn, wl.E, wl.k, wl.capacity_factor, wl.gating, wl.act, wl.dtype,
+                     wl.ep_ranks, wl.placement, wl.n_shared, wl.ffn_shared)
+    w = Weights(w_router=dev(inp.w_router), w1=dev(inp.w1), w2=dev(inp.w2), w_up=dev(inp.w_up),
+                bias=dev(inp.bias), ws_gate=dev(inp.ws_gate), ws_up=dev(inp.ws_up), ws_down=dev(inp.ws_down))
+    x, dy = dev(inp.x), dev(inp.dy)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        layer.step(x, dy, w)
+    torch.cuda.synchronize()
+
+    # 1) whole steps, events only at the ends
+    log(f"[bench] timing {args.steps} steps")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        layer.step(x, dy, w)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # 2) per entry point, events around each call (same stream)
+    stages = [("route", lambda: layer.route(x, w)), ("dispatch", lambda: layer.dispatch(x)),
+              ("ffn_fwd", lambda: layer.experts_fwd(w))]
+    if wl.n_shared:
+        stages.append(("shared_fwd", lambda: layer.shared_fwd(x, w)))
+    stages += [("combine", layer.combine), ("combine_bwd", lambda: layer.combine_bwd(dy)),
+               ("ffn_bwd", lambda: layer.experts_bwd(w))]
+    if wl.n_shared:
+        stages.append(("shared_bwd", lambda: layer.shared_bwd(x, dy, w)))
+    stages += [("route_bwd", lambda: layer.route_bwd(x)), ("dispatch_bwd", lambda: layer.dispatch_bwd(w))]
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        for (name, fn), (a, b) in zip(stages, evs[s]):
+            a.record(st)
+            fn()
+            b.record(st)
+    torch.cuda.synchronize()
+    times = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+             for i, (name, _) in enumerate(stages)}
+
+    n = int(layer.expert_offsets[-1].item())
+    row_of = layer.row_of.view(wl.T, wl.k)
+    T_kept = int((row_of >= 0).any(dim=1).sum().item())
+    alg = algorithmic(wl, n, T_kept)
+    kernels = {}
+    for name, ms in times.items():
+        a = alg[name]
+        ent = {"ms": round(ms, 4)}
+        if "bytes" in a:
+            gbs = a["bytes"] / (ms * 1e-3) / 1e9
+            ent.update(bytes=a["bytes"], GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        else:
+            tf = a["flops"] / (ms * 1e-3) / 1e12
+            ent.update(flops=a["flops"], TFLOPs=round(tf, 1), frac_mfma=round(tf / PEAK_TFLOPS[wl.dtype], 4))
+        kernels[name] = ent
+    gemm_names = [k_ for k_ in ("ffn_fwd", "ffn_bwd", "shared_fwd", "shared_bwd") if k_ in times]
+    gemm_ms = sum(times[k_] for k_ in gemm_names)
+    gemm_flops = sum(alg[k_]["flops"] for k_ in gemm_names)
+    launches = 6 * (2 if wl.n_shared else 1)
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    roofline = {"kernel": f"grouped expert GEMM, fwd+bwd ({launches} launches per step)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "per_step_flops": gemm_flops, "per_step_ms": round(gemm_ms, 4)}
+    permute_gbs = kernels["dispatch"]["GBps"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(wl, inp, args.cpu_tokens)
+
+    result = {
+        "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM % MFMA peak; permute GB/s",
+        "value": round(wl.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "ffn": wl.ffn, "E": wl.E, "k": wl.k,
+                   "capacity_factor": wl.capacity_factor, "gating": wl.gating, "act": wl.act,
+                   "n_shared": wl.n_shared, "ffn_shared": wl.ffn_shared, "ep_ranks": wl.ep_ranks,
+                   "rows_kept": n, "parallelism": "single GPU"},
+        "grouped_gemm_frac_mfma": roofline["frac"],
+        "permute_GBps": permute_gbs,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,218 @@
+/*
+ * libmoe — one GPU's share of a mixture-of-experts layer on AMD MI355X
+ * (gfx950): routing, dispatch into per-expert / per-EP-rank buffers, grouped
+ * expert FFN forward and backward, weighted combine, and the backward duals.
+ *
+ * The problem statement these calls follow is the tutorial chapter
+ * "扩展 MoE 模型——迈向分布式训练" (distributed MoE training):
+ *   - section "专家并行：在不同设备上分配专家", part 二: the four EP steps
+ *     (replicated local gate, send tokens to the expert's device, local
+ *     expert compute, return results in sequence order);
+ *   - section "All-to-All 通信模式", part 二: N devices, T/N tokens and E/N
+ *     experts each, gate g(x), device i sends to device k the set S_ik of its
+ *     tokens whose expert lives on k; part 六: variable-size exchanges;
+ *   - section "专家并行与数据并行的结合", part 三: backward routes gradients
+ *     back to the experts, expert parameter gradients are computed locally;
+ *   - section "用于分布式 MoE 的主流框架与库": the knobs a layer takes (top-k
+ *     gate with k, ffn experts, model width, number of experts, EP size);
+ *   - section "通信优化方法", part 四: pre-allocated, reused buffers.
+ * The Piper summary (方法论 1) names expert capacity and the routing table
+ * as per-GPU quantities.
+ *
+ * Conventions for every call below:
+ *   - Every tensor argument is a DEVICE pointer owned by the caller,
+ *     contiguous and row-major, 16-byte aligned.  The library never
+ *     allocates, frees or synchronises; scratch memory is the caller's
+ *     `ws` buffer of moe_plan()'s workspace_bytes.
+ *   - `stream` is a hipStream_t passed as a plain pointer (NULL = the null
+ *     stream).  Each call validates on the host, enqueues its kernels on
+ *     that stream and returns; results are valid for later work on it.
+ *   - Element type `dtype` (MOE_F32 / MOE_BF16) applies to x, y, weights,
+ *     activations and their gradients ("void*" arguments).  Logits, gate
+ *     weights and their gradients are always fp32; indices and counts int32;
+ *     offsets int64.
+ *   - Return value: MOE_OK, or a negative moe_status.  On MOE_ERR_INVALID /
+ *     MOE_ERR_UNSUPPORTED nothing was enqueued.  On MOE_ERR_HIP a launch
+ *     failed (see moe_last_hip_error()); outputs are then undefined.
+ *   - Results are deterministic: no floating-point atomics are used, so two
+ *     identical calls give bit-identical outputs.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,      /* bad argument: nothing enqueued          */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what is implemented   */
+  MOE_ERR_HIP = -3           /* a HIP launch failed                     */
+} moe_status;
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Gate weight of the j-th chosen expert e_j of a token with logits l. */
+enum {
+  MOE_GATE_SOFTMAX_TOPK = 0,        /* g_j = softmax(l)[e_j]                    */
+  MOE_GATE_SOFTMAX_TOPK_RENORM = 1, /* g_j = softmax(l)[e_j] / sum_m softmax(l)[e_m] */
+  MOE_GATE_TOPK_SOFTMAX = 2         /* g_j = softmax over the k chosen logits   */
+};
+
+enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 };
+
+/* Expert e's EP rank: contiguous e / (E/R) (the tutorial's 4-device
+ * picture: Dev0 holds E0, E1; Dev1 holds E2, E3); round-robin e % R. */
+enum { MOE_PLACE_CONTIGUOUS = 0, MOE_PLACE_ROUND_ROBIN = 1 };
+
+typedef struct {
+  int64_t T;                /* tokens, >= 1                                    */
+  int64_t d;                /* model width, multiple of 8                      */
+  int64_t ffn;              /* routed expert hidden width, multiple of 8       */
+  int64_t E;                /* routed experts, 1..64                           */
+  int64_t k;                /* experts per token, 1..min(E, 8)                 */
+  float capacity_factor;    /* > 0: C = ceil(cf*k*T/E) (double, left to right,
+                               capped at T); <= 0: dropless, C = T             */
+  int32_t gating;           /* MOE_GATE_*                                      */
+  int32_t act;              /* MOE_ACT_*                                       */
+  int32_t dtype;            /* MOE_F32 | MOE_BF16                              */
+  int32_t ep_ranks;         /* R >= 1, E % R == 0                              */
+  int32_t placement;        /* MOE_PLACE_*                                     */
+  int64_t n_shared;         /* always-on shared experts (0 if none)            */
+  int64_t ffn_shared;       /* hidden width of each shared expert              */
+} moe_config;
+
+typedef struct {
+  int64_t C;                /* expert capacity                                 */
+  int64_t n_max;            /* rows of the permuted buffers: min(T*k, E*C)     */
+  size_t workspace_bytes;   /* `ws` size for every call below that takes one   */
+} moe_sizes;
+
+/* Row segments of a grouped expert FFN call.  Routed experts: groups = E,
+ * offsets = moe_dispatch's expert_offsets, rows_max = n_max, ffn = cfg.ffn,
+ * use_placement = 1.  Shared experts: groups = 1, offsets = {0, T},
+ * rows_max = T, ffn = n_shared*ffn_shared, use_placement = 0. */
+typedef struct {
+  int64_t groups;           /* number of row segments, 1..65                    */
+  int64_t ffn;              /* hidden width of every group, multiple of 8       */
+  int64_t rows_max;         /* rows allocated in the row buffers                */
+  const int64_t* offsets;   /* DEVICE [groups+1], ascending, offsets[0] = 0,
+                               offsets[groups] <= rows_max: group g owns rows
+                               [offsets[g], offsets[g+1])                        */
+  int32_t use_placement;    /* 1: group g is send slot g, whose expert (and
+                               weight set) follows cfg's placement; 0: group g
+                               uses weight set g                                */
+} moe_groups;
+
+/* Host only.  Capacity, buffer rows and workspace size for cfg.
+ * Errors: MOE_ERR_INVALID (null pointer, non-positive sizes, k > E,
+ * E % R != 0, unknown enum), MOE_ERR_UNSUPPORTED (E > 64, k > 8, d or ffn
+ * not a multiple of 8). */
+int moe_plan(const moe_config* cfg, moe_sizes* out);
+
+/* Gate GEMM, softmax and top-k routing (tutorial: 专家并行 二 step 1, the
+ * replicated router; 框架: top-k gate).
+ *   x [T, d] dtype; w_router [d, E] dtype; bias [E] fp32 or NULL (added to
+ *   the logits before softmax and selection).
+ *   logits [T, E] fp32: l = x W_r + b, fp32 accumulation.
+ *   topk_idx [T, k] int32: per token, experts ordered by (logit descending,
+ *   index ascending), first k — equal logits go to the lower index.
+ *   topk_w [T, k] fp32: gate weights per cfg->gating. */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router,
+              const float* bias, float* logits, int32_t* topk_idx,
+              float* topk_w, void* stream);
+
+/* Capacity, counts, offsets, EP send layout and permutation (tutorial:
+ * All-to-All 二/六, send sets S_ik of variable size; Piper 方法论 1:
+ * capacity).  pos(t, j) = number of tokens t' < t that chose expert
+ * e = topk_idx[t, j]; the assignment is kept iff pos < C (overflow dropped in
+ * token order).  Send slots list the experts by (EP rank, local index); an
+ * expert's segment lists its kept tokens in ascending order.
+ *   raw_counts [E] int32: tokens that chose e;  expert_counts [E] int32:
+ *     kept, min(raw, C);
+ *   expert_offsets [E+1] int64: segment start of send slot s (slot order);
+ *   send_counts [R] int32 / send_offsets [R+1] int64: rows per EP rank;
+ *   row_of [T*k] int32: row of assignment (t, j), -1 if dropped;
+ *   assign_of_row [n_max] int32: t*k + j of each row (rows >= n untouched);
+ *   x_perm [n_max, d] dtype: x_perm[row_of[t*k+j]] = x[t] (exact copy) —
+ *     the all-to-all send buffer, segment q = rows of EP rank q.
+ *   ws: moe_plan's workspace. */
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                 void* x_perm, int32_t* row_of, int32_t* assign_of_row,
+                 int32_t* raw_counts, int32_t* expert_counts,
+                 int64_t* expert_offsets, int32_t* send_counts,
+                 int64_t* send_offsets, void* ws, void* stream);
+
+/* Grouped expert FFN forward (tutorial: 专家并行 二 step 3, local experts;
+ * 框架: ffn experts), MFMA with fp32 accumulation.
+ *   x_rows [rows_max, d]; weights per expert:
+ *     GELU:   w_in = W1 [E', d, ffn], w_out = W2 [E', ffn, d], w_up NULL;
+ *     SwiGLU: w_in = W_gate, w_up = W_up [E', d, ffn], w_out = W_down.
+ *   act_saved: GELU Z = x W1 [rows_max, ffn]; SwiGLU [rows_max, 2*ffn] with
+ *     A = x W_gate in columns [0, ffn) and B = x W_up in [ffn, 2*ffn).
+ *   h [rows_max, ffn]: GELU(Z) (exact erf form) or silu(A) * B.
+ *   y_rows [rows_max, d]: h W_out.  Rows outside the segments are untouched. */
+int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,
+                       const void* x_rows, const void* w_in, const void* w_up,
+                       const void* w_out, void* act_saved, void* h,
+                       void* y_rows, void* stream);
+
+/* Grouped expert FFN backward (tutorial: 专家并行与数据并行的结合 三.3:
+ * gradients routed back to the experts, parameter gradients computed
+ * locally).  dy_rows [rows_max, d] is dL/d y_rows.
+ *   dx_rows [rows_max, d] = dL/d x_rows;
+ *   dw_in, dw_up, dw_out: same shapes and dtype as w_in, w_up, w_out;
+ *   weight sets with no rows get exact zeros.
+ *   ws: moe_plan's workspace (holds dL/dZ or dL/d[A|B] in dtype). */
+int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp,
+                       const void* x_rows, const void* w_in, const void* w_up,
+                       const void* w_out, const void* act_saved, const void* h,
+                       const void* dy_rows, void* dx_rows, void* dw_in,
+                       void* dw_up, void* dw_out, void* ws, void* stream);
+
+/* Weighted combine (tutorial: 专家并行 二 step 4, results returned in
+ * sequence order; 流水线并行 三: outputs merged).
+ *   y[t] = sum over kept j of topk_w[t, j] * y_perm[row_of[t*k+j]]
+ *          (+ y_shared[t] if y_shared != NULL), fp32 accumulation.
+ *   A token with every choice dropped gets y = 0 (+ shared). */
+int moe_combine(const moe_config* cfg, const void* y_perm,
+                const int32_t* row_of, const float* topk_w,
+                const void* y_shared, void* y, void* stream);
+
+/* Combine backward.  dy_perm[row_of[t*k+j]] = topk_w[t, j] * dy[t];
+ * d_topk_w[t, j] = <dy[t], y_perm[row_of[t*k+j]]> (0 if dropped). */
+int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* y_perm,
+                    const int32_t* row_of, const float* topk_w, void* dy_perm,
+                    float* d_topk_w, void* stream);
+
+/* Router backward (tutorial: 专家并行与数据并行的结合 三.4, router
+ * gradients).  dlogits [T, E] fp32 through the gate-weight Jacobian:
+ *   SOFTMAX_TOPK: dl = p (dp - <p, dp>), dp[e_j] = d_topk_w[t, j], else 0;
+ *   RENORM / TOPK_SOFTMAX: dl[e_j] = g_j (dg_j - sum_m g_m dg_m), 0 elsewhere.
+ * dw_router [d, E] dtype = x^T dlogits (deterministic two-stage reduction).
+ * The bias gets no gradient.  ws: moe_plan's workspace. */
+int moe_route_bwd(const moe_config* cfg, const void* x, const float* logits,
+                  const int32_t* topk_idx, const float* d_topk_w,
+                  float* dlogits, void* dw_router, void* ws, void* stream);
+
+/* Dispatch backward (un-permute and sum, router dx fused):
+ *   dx[t] = sum over kept j of dx_perm[row_of[t*k+j]]
+ *           + sum_e dlogits[t, e] * w_router[:, e]
+ *           (+ dx_add[t] if dx_add != NULL, e.g. the shared experts' dx). */
+int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm,
+                     const int32_t* row_of, const float* dlogits,
+                     const void* w_router, const void* dx_add, void* dx,
+                     void* stream);
+
+const char* moe_status_string(int status);
+/* hipError_t of the last MOE_ERR_HIP on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_MOE_H */

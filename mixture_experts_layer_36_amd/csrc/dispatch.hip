@@ -1,0 +1,195 @@
+// Capacity, counts, EP send layout and token permutation.
+//
+// Follows the tutorial ch.4 "All-to-All 通信模式" part 二 (device i sends to
+// device k the set S_ik of its tokens whose expert lives on k) and part 六
+// (those sets have different sizes), and the Piper summary's 方法论 1
+// (expert capacity).  Position of assignment (t, j) in its expert's buffer:
+// pos = number of tokens t' < t that chose the same expert; it is kept iff
+// pos < C, so overflow is dropped in token order.
+//
+// Stable positions without order-dependent atomics, in four launches:
+//   1. block_hist: per block of 256 tokens, count the tokens choosing each
+//      expert (integer LDS atomics: the count does not depend on order);
+//   2. scan: one workgroup turns the block counts into per-(block, expert)
+//      bases, raw / kept counts, slot offsets and send segments;
+//   3. rows: per block, each token's rank among the block's earlier tokens
+//      (64-bit wave ballots + popcount, then a prefix over the 4 waves) gives
+//      pos, the kept flag, the row, row_of and assign_of_row;
+//   4. copy: each kept token row is read once and written to its <= k rows
+//      (16-byte loads / stores, coalesced along the row).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(kDispatchBlock) void block_hist_kernel(const int32_t* __restrict__ idx, int64_t Tn,
+                                                                    int E, int k, int32_t* __restrict__ block_counts) {
+  __shared__ int cnt[64];
+  const int tid = threadIdx.x;
+  if (tid < 64) cnt[tid] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kDispatchBlock + tid;
+  if (t < Tn) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  if (tid < E) block_counts[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__device__ __forceinline__ int slot_expert(int s, int E, int R, int placement) {
+  const int L = E / R;
+  return placement == 0 ? s : (s % L) * R + s / L;
+}
+
+__global__ __launch_bounds__(64) void scan_kernel(const int32_t* __restrict__ block_counts, int nb, int E, int64_t C,
+                                                  int R, int placement, int32_t* __restrict__ block_base,
+                                                  int32_t* __restrict__ raw_counts, int32_t* __restrict__ kept_counts,
+                                                  int64_t* __restrict__ slot_offsets, int32_t* __restrict__ send_counts,
+                                                  int64_t* __restrict__ send_offsets,
+                                                  int64_t* __restrict__ expert_start) {
+  __shared__ int64_t kept_s[64];
+  const int e = threadIdx.x;
+  if (e < E) {
+    int64_t run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i = (int64_t)b * E + e;
+      const int c = block_counts[i];
+      block_base[i] = (int32_t)run;
+      run += c;
+    }
+    raw_counts[e] = (int32_t)run;
+    const int64_t kept = run < C ? run : C;
+    kept_counts[e] = (int32_t)kept;
+    kept_s[e] = kept;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int64_t off = 0;
+    for (int s = 0; s < E; ++s) {
+      const int ex = slot_expert(s, E, R, placement);
+      slot_offsets[s] = off;
+      expert_start[ex] = off;
+      off += kept_s[ex];
+    }
+    slot_offsets[E] = off;
+    const int L = E / R;
+    for (int q = 0; q < R; ++q) {
+      send_offsets[q] = slot_offsets[q * L];
+      send_counts[q] = (int32_t)(slot_offsets[(q + 1) * L] - slot_offsets[q * L]);
+    }
+    send_offsets[R] = off;
+  }
+}
+
+__global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
+    const int32_t* __restrict__ idx, int64_t Tn, int E, int k, int64_t C, const int32_t* __restrict__ block_base,
+    const int64_t* __restrict__ expert_start, int32_t* __restrict__ row_of, int32_t* __restrict__ assign_of_row) {
+  constexpr int NW = kDispatchBlock / 64;
+  __shared__ int wave_cnt[NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kDispatchBlock + tid;
+  int my_e[8];
+  int rank[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    my_e[j] = (j < k && t < Tn) ? idx[t * k + j] : -1;
+    rank[j] = 0;
+  }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int e = 0; e < E; ++e) {
+    bool c = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c |= (my_e[j] == e);
+    const unsigned long long mask = __ballot(c);
+    const int before = __popcll(mask & lt);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (my_e[j] == e) rank[j] = before;
+    if (lane == 0) wave_cnt[w][e] = __popcll(mask);
+  }
+  __syncthreads();
+  if (t >= Tn) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const int e = my_e[j];
+    int32_t row = -1;
+    if (e >= 0 && e < E) {
+      int prefix = 0;
+      for (int ww = 0; ww < w; ++ww) prefix += wave_cnt[ww][e];
+      const int64_t pos = (int64_t)block_base[(int64_t)blockIdx.x * E + e] + prefix + rank[j];
+      if (pos < C) {
+        row = (int32_t)(expert_start[e] + pos);
+        assign_of_row[row] = (int32_t)(t * k + j);
+      }
+    }
+    row_of[t * k + j] = row;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void permute_copy_kernel(const T* __restrict__ x, const int32_t* __restrict__ row_of,
+                                                           T* __restrict__ x_perm, int64_t Tn, int d, int k,
+                                                           int tpb) {
+  constexpr int V = Vec16<T>::N;
+  const int nch = d / V;
+  const int total = tpb * nch;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int i = threadIdx.x; i < total; i += 256) {
+    const int tl = i / nch, c = i - tl * nch;
+    const int64_t t = t0 + tl;
+    if (t >= Tn) break;
+    int rows[8];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rows[j] = j < k ? row_of[t * k + j] : -1;
+      any |= rows[j] >= 0;
+    }
+    if (!any) continue;
+    const u32x4 v = ld16(x + t * d + (int64_t)c * V);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (rows[j] >= 0) st16(x_perm + (int64_t)rows[j] * d + (int64_t)c * V, v);
+  }
+}
+
+int tokens_per_copy_block(int64_t d, int elem_bytes) {
+  const int64_t nch = d * elem_bytes / 16;
+  int64_t tpb = (256 * 8) / (nch > 0 ? nch : 1);
+  if (tpb < 1) tpb = 1;
+  if (tpb > 64) tpb = 64;
+  return (int)tpb;
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st) {
+  const int nb = (int)((a.T + kDispatchBlock - 1) / kDispatchBlock);
+  hipLaunchKernelGGL(block_hist_kernel, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E, a.k,
+                     a.block_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, st, a.block_counts, nb, a.E, a.C, a.R, a.placement,
+                     a.block_base, a.raw_counts, a.expert_counts, a.expert_offsets, a.send_counts, a.send_offsets,
+                     a.expert_start);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_rows_kernel, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E, a.k, a.C,
+                     a.block_base, a.expert_start, a.row_of, a.assign_of_row);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int eb = bf16_dtype ? 2 : 4;
+  const int tpb = tokens_per_copy_block(a.d, eb);
+  const int64_t blocks = (a.T + tpb - 1) / tpb;
+  if (bf16_dtype)
+    hipLaunchKernelGGL((permute_copy_kernel<bf16>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)a.x,
+                       a.row_of, (bf16*)a.x_perm, a.T, (int)a.d, a.k, tpb);
+  else
+    hipLaunchKernelGGL((permute_copy_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st, (const float*)a.x,
+                       a.row_of, (float*)a.x_perm, a.T, (int)a.d, a.k, tpb);
+  return hipGetLastError();
+}
+
+}  // namespace moe

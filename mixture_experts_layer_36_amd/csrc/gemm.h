@@ -1,0 +1,43 @@
+// Grouped expert GEMM launch interface (internal to libmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+namespace gemm {
+
+enum { KIND_FWD = 0, KIND_DGRAD = 1 };
+enum {
+  EPI_STORE = 0,         // C = acc
+  EPI_GELU_FWD = 1,      // C = Z = acc, C2 = GELU(Z)
+  EPI_SWIGLU_FWD = 2,    // tile pairs gate|up columns: C[:, f] = A, C[:, c_split+f] = B, C2 = silu(A)*B
+  EPI_GELU_BWD = 3,      // C = acc * GELU'(X1)
+  EPI_SWIGLU_BWD = 4,    // X1 = [A|B]; C[:, f] = dA, C[:, c_split+f] = dB with dH = acc
+  EPI_STORE_SPLITN = 5   // wgrad: columns >= c_split go to C2
+};
+
+struct Args {
+  const void* A = nullptr;  int64_t lda = 0;
+  const void* B = nullptr;  const void* B2 = nullptr;
+  int64_t ldb = 0;          // row stride of B (and B2)
+  int64_t b_gstride = 0;    // elements between consecutive weight sets
+  int64_t b_split = 0;      // DGRAD: K >= b_split reads B2 at K - b_split
+  void* C = nullptr;        void* C2 = nullptr;
+  int64_t ldc = 0, ldc2 = 0;
+  int64_t c_gstride = 0;    // WGRAD: elements between consecutive weight sets
+  int64_t c_split = 0;
+  const void* X1 = nullptr; int64_t ldx = 0;
+  int64_t M = 0, N = 0, K = 0;
+  const int64_t* offsets = nullptr;  // device [groups+1]
+  int groups = 0;
+  int rr_R = 0, rr_L = 1;   // round-robin slot -> expert map (rr_R = 0: identity)
+  int tiles_m = 0, tiles_n = 0;
+};
+
+template <typename T>
+hipError_t run_rows(int kind, int epi, const Args& a, int64_t rows_max, hipStream_t st);
+template <typename T>
+hipError_t run_wgrad(int epi, const Args& a, hipStream_t st);
+
+}  // namespace gemm
+}  // namespace moe

@@ -1,0 +1,55 @@
+// Launch interface of libmoe's bandwidth / routing kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kDispatchBlock = 256;  // tokens per block of the stable-rank kernels
+
+struct RouteArgs {
+  const void* x; const void* w; const float* bias;
+  float* logits; int32_t* topk_idx; float* topk_w;
+  int64_t T; int d; int E; int k; int gating;
+};
+
+struct DispatchArgs {
+  const void* x; const int32_t* topk_idx;
+  void* x_perm; int32_t* row_of; int32_t* assign_of_row;
+  int32_t* raw_counts; int32_t* expert_counts; int64_t* expert_offsets;
+  int32_t* send_counts; int64_t* send_offsets;
+  // workspace
+  int32_t* block_counts; int32_t* block_base; int64_t* expert_start;
+  int64_t T; int64_t d; int E; int k; int64_t C; int R; int placement;
+};
+
+struct CombineArgs {
+  const void* y_perm; const int32_t* row_of; const float* topk_w;
+  const void* y_shared; void* y;                 // forward
+  const void* dy; void* dy_perm; float* d_topk_w; // backward
+  int64_t T; int64_t d; int k;
+};
+
+struct RouteBwdArgs {
+  const void* x; const float* logits; const int32_t* topk_idx; const float* d_topk_w;
+  float* dlogits; void* dw_router; float* partial;
+  int64_t T; int64_t d; int E; int k; int gating;
+};
+
+struct DispatchBwdArgs {
+  const void* dx_perm; const int32_t* row_of; const float* dlogits; const void* w_router;
+  const void* dx_add; void* dx;
+  int64_t T; int64_t d; int E; int k;
+};
+
+hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st);
+
+int tokens_per_copy_block(int64_t d, int elem_bytes);
+int router_wgrad_blocks(int64_t T);
+
+}  // namespace moe

@@ -1,0 +1,317 @@
+// libmoe C ABI: argument validation, sizing and kernel launches.
+// The contract of every entry point is documented in include/moe.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID;
+  if (c->T <= 0 || c->d <= 0 || c->ffn <= 0 || c->E <= 0 || c->k <= 0) return MOE_ERR_INVALID;
+  if (c->k > c->E) return MOE_ERR_INVALID;
+  if (c->gating < MOE_GATE_SOFTMAX_TOPK || c->gating > MOE_GATE_TOPK_SOFTMAX) return MOE_ERR_INVALID;
+  if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (c->ep_ranks < 1 || c->E % c->ep_ranks != 0) return MOE_ERR_INVALID;
+  if (c->placement != MOE_PLACE_CONTIGUOUS && c->placement != MOE_PLACE_ROUND_ROBIN) return MOE_ERR_INVALID;
+  if (c->n_shared < 0 || (c->n_shared > 0 && c->ffn_shared <= 0)) return MOE_ERR_INVALID;
+  if (!(c->capacity_factor == c->capacity_factor)) return MOE_ERR_INVALID;  // NaN
+  if (c->E > 64 || c->k > 8) return MOE_ERR_UNSUPPORTED;
+  if (c->d % 8 != 0 || c->ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 0 && (c->n_shared * c->ffn_shared) % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->T * c->k >= (int64_t)1 << 31 || c->T >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (c->d >= (int64_t)1 << 24 || c->ffn >= (int64_t)1 << 24) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_config* c) {
+  const double cf = (double)c->capacity_factor;
+  if (cf <= 0.0) return c->T;
+  const double v = ceil(cf * (double)c->k * (double)c->T / (double)c->E);
+  return v >= (double)c->T ? c->T : (int64_t)v;
+}
+
+size_t elem_bytes(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+struct WsLayout {
+  size_t dispatch, route_bwd, ffn_routed, ffn_shared, total;
+};
+
+WsLayout ws_layout(const moe_config* c, int64_t n_max) {
+  WsLayout w;
+  const int64_t nb = (c->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
+  w.dispatch = round_up((size_t)nb * c->E * 4, 256) * 2 + round_up((size_t)c->E * 8, 256);
+  w.route_bwd = round_up((size_t)moe::router_wgrad_blocks(c->T) * c->d * c->E * 4, 256);
+  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  w.ffn_routed = round_up((size_t)n_max * m * c->ffn * elem_bytes(c), 256);
+  w.ffn_shared = c->n_shared > 0 ? round_up((size_t)c->T * m * c->n_shared * c->ffn_shared * elem_bytes(c), 256) : 0;
+  w.total = w.dispatch;
+  if (w.route_bwd > w.total) w.total = w.route_bwd;
+  if (w.ffn_routed > w.total) w.total = w.ffn_routed;
+  if (w.ffn_shared > w.total) w.total = w.ffn_shared;
+  return w;
+}
+
+int check_groups(const moe_config* c, const moe_groups* g) {
+  if (!g || !g->offsets) return MOE_ERR_INVALID;
+  if (g->groups < 1 || g->ffn <= 0 || g->rows_max < 0) return MOE_ERR_INVALID;
+  if (g->use_placement && g->groups != c->E) return MOE_ERR_INVALID;
+  if (g->groups > 65) return MOE_ERR_UNSUPPORTED;
+  if (g->ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (g->rows_max >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+void fill_placement(const moe_config* c, const moe_groups* g, moe::gemm::Args& a) {
+  a.groups = (int)g->groups;
+  a.offsets = g->offsets;
+  if (g->use_placement && c->placement == MOE_PLACE_ROUND_ROBIN && c->ep_ranks > 1) {
+    a.rr_R = c->ep_ranks;
+    a.rr_L = (int)(c->E / c->ep_ranks);
+  } else {
+    a.rr_R = 0;
+    a.rr_L = 1;
+  }
+}
+
+template <typename T>
+hipError_t ffn_fwd(const moe_config* c, const moe_groups* g, const void* x, const void* w_in, const void* w_up,
+                   const void* w_out, void* act_saved, void* h, void* y, hipStream_t st) {
+  using namespace moe::gemm;
+  const int64_t d = c->d, F = g->ffn;
+  const bool swiglu = c->act == MOE_ACT_SWIGLU;
+  Args a1;
+  fill_placement(c, g, a1);
+  a1.A = x; a1.lda = d;
+  a1.B = w_in; a1.B2 = swiglu ? w_up : nullptr; a1.ldb = F; a1.b_gstride = d * F;
+  a1.N = F; a1.K = d;
+  a1.C = act_saved; a1.C2 = h; a1.ldc2 = F;
+  if (swiglu) { a1.ldc = 2 * F; a1.c_split = F; } else { a1.ldc = F; }
+  hipError_t e = run_rows<T>(KIND_FWD, swiglu ? EPI_SWIGLU_FWD : EPI_GELU_FWD, a1, g->rows_max, st);
+  if (e != hipSuccess) return e;
+  Args a2;
+  fill_placement(c, g, a2);
+  a2.A = h; a2.lda = F;
+  a2.B = w_out; a2.ldb = d; a2.b_gstride = F * d;
+  a2.N = d; a2.K = F;
+  a2.C = y; a2.ldc = d;
+  return run_rows<T>(KIND_FWD, EPI_STORE, a2, g->rows_max, st);
+}
+
+template <typename T>
+hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, const void* w_in, const void* w_up,
+                   const void* w_out, const void* act_saved, const void* h, const void* dy, void* dx, void* dw_in,
+                   void* dw_up, void* dw_out, void* ws, hipStream_t st) {
+  using namespace moe::gemm;
+  const int64_t d = c->d, F = g->ffn;
+  const bool swiglu = c->act == MOE_ACT_SWIGLU;
+  const int64_t m = swiglu ? 2 : 1;
+  // 1. dgrad through W_out with the activation backward fused: d_act in ws
+  Args a1;
+  fill_placement(c, g, a1);
+  a1.A = dy; a1.lda = d;
+  a1.B = w_out; a1.ldb = d; a1.b_gstride = F * d;
+  a1.N = F; a1.K = d;
+  a1.X1 = act_saved; a1.ldx = m * F;
+  a1.C = ws; a1.ldc = m * F; a1.c_split = F;
+  hipError_t e = run_rows<T>(KIND_DGRAD, swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, a1, g->rows_max, st);
+  if (e != hipSuccess) return e;
+  // 2. dgrad through W_in (and W_up): dx = d_act . [W_in | W_up]^T
+  Args a2;
+  fill_placement(c, g, a2);
+  a2.A = ws; a2.lda = m * F;
+  a2.B = w_in; a2.B2 = swiglu ? w_up : nullptr; a2.ldb = F; a2.b_gstride = d * F;
+  a2.b_split = swiglu ? F : 0;
+  a2.N = d; a2.K = m * F;
+  a2.C = dx; a2.ldc = d;
+  e = run_rows<T>(KIND_DGRAD, EPI_STORE, a2, g->rows_max, st);
+  if (e != hipSuccess) return e;
+  // 3. dW_out = h^T dy
+  Args a3;
+  fill_placement(c, g, a3);
+  a3.A = h; a3.lda = F; a3.M = F;
+  a3.B = dy; a3.ldb = d; a3.N = d;
+  a3.C = dw_out; a3.ldc = d; a3.c_gstride = F * d;
+  e = run_wgrad<T>(EPI_STORE, a3, st);
+  if (e != hipSuccess) return e;
+  // 4. dW_in (| dW_up) = x^T d_act
+  Args a4;
+  fill_placement(c, g, a4);
+  a4.A = x; a4.lda = d; a4.M = d;
+  a4.B = ws; a4.ldb = m * F; a4.N = m * F;
+  a4.C = dw_in; a4.C2 = swiglu ? dw_up : nullptr; a4.ldc = F; a4.c_gstride = d * F;
+  a4.c_split = F;
+  return run_wgrad<T>(swiglu ? EPI_STORE_SPLITN : EPI_STORE, a4, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_plan(const moe_config* cfg, moe_sizes* out) {
+  const int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!out) return MOE_ERR_INVALID;
+  out->C = capacity_of(cfg);
+  const int64_t tk = cfg->T * cfg->k, ec = cfg->E * out->C;
+  out->n_max = tk < ec ? tk : ec;
+  out->workspace_bytes = ws_layout(cfg, out->n_max).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias, float* logits,
+              int32_t* topk_idx, float* topk_w, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!x || !w_router || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID;
+  if (!aligned16(x)) return MOE_ERR_INVALID;
+  moe::RouteArgs a{x, w_router, bias, logits, topk_idx, topk_w, cfg->T, (int)cfg->d, (int)cfg->E, (int)cfg->k,
+                   cfg->gating};
+  return hip_status(moe::launch_route(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm, int32_t* row_of,
+                 int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts, int64_t* expert_offsets,
+                 int32_t* send_counts, int64_t* send_offsets, void* ws, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!x || !topk_idx || !x_perm || !row_of || !assign_of_row || !raw_counts || !expert_counts || !expert_offsets ||
+      !send_counts || !send_offsets || !ws)
+    return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(x_perm) || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID;
+  const int64_t nb = (cfg->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
+  char* w = (char*)ws;
+  const size_t cnt_bytes = round_up((size_t)nb * cfg->E * 4, 256);
+  moe::DispatchArgs a;
+  a.x = x; a.topk_idx = topk_idx; a.x_perm = x_perm; a.row_of = row_of; a.assign_of_row = assign_of_row;
+  a.raw_counts = raw_counts; a.expert_counts = expert_counts; a.expert_offsets = expert_offsets;
+  a.send_counts = send_counts; a.send_offsets = send_offsets;
+  a.block_counts = (int32_t*)w;
+  a.block_base = (int32_t*)(w + cnt_bytes);
+  a.expert_start = (int64_t*)(w + 2 * cnt_bytes);
+  a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k; a.C = capacity_of(cfg);
+  a.R = cfg->ep_ranks; a.placement = cfg->placement;
+  return hip_status(moe::launch_dispatch(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* w_in,
+                       const void* w_up, const void* w_out, void* act_saved, void* h, void* y_rows, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  s = check_groups(cfg, grp);
+  if (s != MOE_OK) return s;
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  if (!x_rows || !w_in || !w_out || !act_saved || !h || !y_rows || (swiglu && !w_up)) return MOE_ERR_INVALID;
+  if (!aligned16(x_rows) || !aligned16(w_in) || !aligned16(w_out) || !aligned16(act_saved) || !aligned16(h) ||
+      !aligned16(y_rows) || (swiglu && !aligned16(w_up)))
+    return MOE_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MOE_BF16 ? ffn_fwd<moe::bf16>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, y_rows, st)
+                                        : ffn_fwd<float>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, y_rows, st);
+  return hip_status(e);
+}
+
+int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* w_in,
+                       const void* w_up, const void* w_out, const void* act_saved, const void* h, const void* dy_rows,
+                       void* dx_rows, void* dw_in, void* dw_up, void* dw_out, void* ws, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  s = check_groups(cfg, grp);
+  if (s != MOE_OK) return s;
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  if (!x_rows || !w_in || !w_out || !act_saved || !h || !dy_rows || !dx_rows || !dw_in || !dw_out || !ws ||
+      (swiglu && (!w_up || !dw_up)))
+    return MOE_ERR_INVALID;
+  const void* ptrs[] = {x_rows, w_in, w_out, act_saved, h, dy_rows, dx_rows, dw_in, dw_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID;
+  if (swiglu && (!aligned16(w_up) || !aligned16(dw_up))) return MOE_ERR_INVALID;
+  if ((uintptr_t)ws & 255u) return MOE_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MOE_BF16
+                     ? ffn_bwd<moe::bf16>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,
+                                          dw_up, dw_out, ws, st)
+                     : ffn_bwd<float>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,
+                                      dw_up, dw_out, ws, st);
+  return hip_status(e);
+}
+
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of, const float* topk_w,
+                const void* y_shared, void* y, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!y_perm || !row_of || !topk_w || !y) return MOE_ERR_INVALID;
+  if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID;
+  moe::CombineArgs a{};
+  a.y_perm = y_perm; a.row_of = row_of; a.topk_w = topk_w; a.y_shared = y_shared; a.y = y;
+  a.T = cfg->T; a.d = cfg->d; a.k = (int)cfg->k;
+  return hip_status(moe::launch_combine(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* y_perm, const int32_t* row_of,
+                    const float* topk_w, void* dy_perm, float* d_topk_w, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!dy || !y_perm || !row_of || !topk_w || !dy_perm || !d_topk_w) return MOE_ERR_INVALID;
+  if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(dy_perm)) return MOE_ERR_INVALID;
+  moe::CombineArgs a{};
+  a.dy = dy; a.y_perm = y_perm; a.row_of = row_of; a.topk_w = topk_w; a.dy_perm = dy_perm; a.d_topk_w = d_topk_w;
+  a.T = cfg->T; a.d = cfg->d; a.k = (int)cfg->k;
+  return hip_status(moe::launch_combine_bwd(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_route_bwd(const moe_config* cfg, const void* x, const float* logits, const int32_t* topk_idx,
+                  const float* d_topk_w, float* dlogits, void* dw_router, void* ws, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!x || !logits || !topk_idx || !d_topk_w || !dlogits || !dw_router || !ws) return MOE_ERR_INVALID;
+  if ((uintptr_t)ws & 255u) return MOE_ERR_INVALID;
+  moe::RouteBwdArgs a{};
+  a.x = x; a.logits = logits; a.topk_idx = topk_idx; a.d_topk_w = d_topk_w; a.dlogits = dlogits;
+  a.dw_router = dw_router; a.partial = (float*)ws;
+  a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k; a.gating = cfg->gating;
+  return hip_status(moe::launch_route_bwd(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm, const int32_t* row_of, const float* dlogits,
+                     const void* w_router, const void* dx_add, void* dx, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!dx_perm || !row_of || !dlogits || !w_router || !dx) return MOE_ERR_INVALID;
+  if (!aligned16(dx_perm) || !aligned16(dx) || (dx_add && !aligned16(dx_add))) return MOE_ERR_INVALID;
+  moe::DispatchBwdArgs a{};
+  a.dx_perm = dx_perm; a.row_of = row_of; a.dlogits = dlogits; a.w_router = w_router; a.dx_add = dx_add; a.dx = dx;
+  a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k;
+  return hip_status(moe::launch_dispatch_bwd(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+"""One MoE layer step through libmoe: buffers plus the call sequence.
+
+``MoELayer`` allocates every output and scratch buffer once (torch device
+memory, following the "pre-allocate and reuse buffers" advice of the
+tutorial's 通信优化方法 section) and issues the C entry points in order:
+
+  forward : moe_route -> moe_dispatch -> moe_expert_ffn_fwd (routed, then
+            shared experts) -> moe_combine
+  backward: moe_combine_bwd -> moe_expert_ffn_bwd (routed, then shared)
+            -> moe_route_bwd -> moe_dispatch_bwd
+
+All of it is enqueued on one stream with no host synchronisation.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import api
+from ._native import make_config, plan
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Weights:
+    w_router: torch.Tensor                 # [d, E]
+    w1: torch.Tensor                       # [E, d, F]  (W1 or W_gate)
+    w2: torch.Tensor                       # [E, F, d]  (W2 or W_down)
+    w_up: Optional[torch.Tensor] = None    # [E, d, F]  (SwiGLU)
+    bias: Optional[torch.Tensor] = None    # [E] fp32
+    ws_gate: Optional[torch.Tensor] = None  # [d, n_shared*Fs]
+    ws_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None  # [n_shared*Fs, d]
+
+
+class MoELayer:
+    def __init__(self, T, d, ffn, E, k, capacity_factor, gating, act, dtype, ep_ranks=1,
+                 placement="contiguous", n_shared=0, ffn_shared=0, device="cuda"):
+        self.cfg = make_config(T, d, ffn, E, k, capacity_factor, gating, act, dtype, ep_ranks,
+                               placement, n_shared, ffn_shared)
+        self.sizes = plan(self.cfg)
+        self.T, self.d, self.F, self.E, self.k = T, d, ffn, E, k
+        self.R = ep_ranks
+        self.act = act
+        self.n_shared = n_shared
+        self.Fs = n_shared * ffn_shared
+        dt = TORCH_DTYPES[dtype]
+        self.dtype = dt
+        dev = torch.device(device)
+        self.device = dev
+        n = self.sizes.n_max
+        m = 2 if act == "swiglu" else 1
+        e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)  # noqa: E731
+        # forward outputs
+        self.logits = e(T, E, dtype=torch.float32)
+        self.topk_idx = e(T, k, dtype=torch.int32)
+        self.topk_w = e(T, k, dtype=torch.float32)
+        self.x_perm = e(max(n, 1), d)
+        self.row_of = e(T * k, dtype=torch.int32)
+        self.assign_of_row = e(max(n, 1), dtype=torch.int32)
+        self.raw_counts = e(E, dtype=torch.int32)
+        self.expert_counts = e(E, dtype=torch.int32)
+        self.expert_offsets = e(E + 1, dtype=torch.int64)
+        self.send_counts = e(ep_ranks, dtype=torch.int32)
+        self.send_offsets = e(ep_ranks + 1, dtype=torch.int64)
+        self.act_saved = e(max(n, 1), m * ffn)
+        self.h = e(max(n, 1), ffn)
+        self.y_perm = e(max(n, 1), d)
+        self.y = e(T, d)
+        # backward outputs
+        self.dy_perm = e(max(n, 1), d)
+        self.d_topk_w = e(T, k, dtype=torch.float32)
+        self.dx_perm = e(max(n, 1), d)
+        self.dw1 = e(E, d, ffn)
+        self.dw_up = e(E, d, ffn) if act == "swiglu" else None
+        self.dw2 = e(E, ffn, d)
+        self.dlogits = e(T, E, dtype=torch.float32)
+        self.dw_router = e(d, E)
+        self.dx = e(T, d)
+        if n_shared > 0:
+            self.s_offsets = torch.tensor([0, T], dtype=torch.int64, device=dev)
+            self.s_act = e(T, m * self.Fs)
+            self.s_h = e(T, self.Fs)
+            self.y_shared = e(T, d)
+            self.dx_shared = e(T, d)
+            self.dws_gate = e(d, self.Fs)
+            self.dws_up = e(d, self.Fs) if act == "swiglu" else None
+            self.dws_down = e(self.Fs, d)
+        self.ws = e(max(1, (self.sizes.workspace_bytes + 255) // 256 * 256), dtype=torch.uint8)
+        self.grp = api.groups(E, ffn, n, self.expert_offsets, use_placement=True)
+        if n_shared > 0:
+            self.sgrp = api.groups(1, self.Fs, T, self.s_offsets, use_placement=False)
+
+    # ------------------------------------------------------------------ steps
+    def route(self, x, w: Weights):
+        api.moe_route(self.cfg, x, w.w_router, w.bias, self.logits, self.topk_idx, self.topk_w)
+
+    def dispatch(self, x):
+        api.moe_dispatch(self.cfg, x, self.topk_idx, self.x_perm, self.row_of, self.assign_of_row,
+                         self.raw_counts, self.expert_counts, self.expert_offsets, self.send_counts,
+                         self.send_offsets, self.ws)
+
+    def experts_fwd(self, w: Weights):
+        api.moe_expert_ffn_fwd(self.cfg, self.grp, self.x_perm, w.w1, w.w_up, w.w2, self.act_saved,
+                               self.h, self.y_perm)
+
+    def shared_fwd(self, x, w: Weights):
+        api.moe_expert_ffn_fwd(self.cfg, self.sgrp, x, w.ws_gate, w.ws_up, w.ws_down, self.s_act,
+                               self.s_h, self.y_shared)
+
+    def combine(self):
+        api.moe_combine(self.cfg, self.y_perm, self.row_of, self.topk_w,
+                        self.y_shared if self.n_shared else None, self.y)
+
+    def combine_bwd(self, dy):
+        api.moe_combine_bwd(self.cfg, dy, self.y_perm, self.row_of, self.topk_w, self.dy_perm,
+                            self.d_topk_w)
+
+    def experts_bwd(self, w: Weights):
+        api.moe_expert_ffn_bwd(self.cfg, self.grp, self.x_perm, w.w1, w.w_up, w.w2, self.act_saved,
+                               self.h, self.dy_perm, self.dx_perm, self.dw1, self.dw_up, self.dw2,
+                               self.ws)
+
+    def shared_bwd(self, x, dy, w: Weights):
+        api.moe_expert_ffn_bwd(self.cfg, self.sgrp, x, w.ws_gate, w.ws_up, w.ws_down, self.s_act,
+                               self.s_h, dy, self.dx_shared, self.dws_gate, self.dws_up,
+                               self.dws_down, self.ws)
+
+    def route_bwd(self, x):
+        api.moe_route_bwd(self.cfg, x, self.logits, self.topk_idx, self.d_topk_w, self.dlogits,
+                          self.dw_router, self.ws)
+
+    def dispatch_bwd(self, w: Weights):
+        api.moe_dispatch_bwd(self.cfg, self.dx_perm, self.row_of, self.dlogits, w.w_router,
+                             self.dx_shared if self.n_shared else None, self.dx)
+
+    def forward(self, x, w: Weights):
+        self.route(x, w)
+        self.dispatch(x)
+        self.experts_fwd(w)
+        if self.n_shared:
+            self.shared_fwd(x, w)
+        self.combine()
+        return self.y
+
+    def backward(self, x, dy, w: Weights):
+        self.combine_bwd(dy)
+        self.experts_bwd(w)
+        if self.n_shared:
+            self.shared_bwd(x, dy, w)
+        self.route_bwd(x)
+        self.dispatch_bwd(w)
+        return self.dx
+
+    def step(self, x, dy, w: Weights):
+        self.forward(x, w)
+        self.backward(x, dy, w)

@@ -9,4 +9,4 @@ numpy arrays: fp32 tensors as ``float32``, bf16 tensors as their raw 16-bit
 patterns in ``uint16`` arrays.
 """
 from .workloads import WORKLOADS, Workload, workload, zipf_bias  # noqa: F401
-from .tensors import LayerInputs, make_inputs, normal  # noqa: F401
+from .tensors import LayerInputs, dyadic, make_inputs, normal  # noqa: F401

@@ -91,12 +91,39 @@ class LayerInputs:
     dy: np.ndarray
 
 
-def make_inputs(wl: Workload, with_dy: bool = True) -> LayerInputs:
+def _f32_to_storage_exact(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    bits = a.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("value not representable in bf16")
+    return (bits >> 16).astype(np.uint16)
+
+
+def dyadic(seed: int, shape, dtype: str, step: float, lim: float) -> np.ndarray:
+    """Seeded values on the grid step*Z, clipped to [-lim, lim]: small
+    dyadic numbers whose sums are exact in fp32 (used to force exactly
+    equal logits, i.e. ties)."""
+    z = normal(seed, shape, "f32", 1.0).astype(np.float64)
+    v = np.clip(np.round(z / step) * step, -lim, lim)
+    return _f32_to_storage_exact(v, dtype)
+
+
+def make_inputs(wl: Workload, with_dy: bool = True, dyadic_router: bool = False) -> LayerInputs:
+    """Inputs of a workload.  With ``dyadic_router`` the tokens are small
+    integers in [-3, 3] and the router weights multiples of 1/2 in [-2, 2]:
+    every logit is then exact in fp32 whatever the summation order, and equal
+    logits (ties) are frequent."""
     s = wl.seed
     dt = wl.dtype
     T, d, F, E = wl.T, wl.d, wl.ffn, wl.E
-    x = normal(s ^ 1, (T, d), dt, 1.0)
-    w_router = normal(s ^ 2, (d, E), dt, wl.w_std)
+    if dyadic_router:
+        x = dyadic(s ^ 1, (T, d), dt, 1.0, 3.0)
+        w_router = dyadic(s ^ 2, (d, E), dt, 0.5, 2.0)
+    else:
+        x = normal(s ^ 1, (T, d), dt, 1.0)
+        w_router = normal(s ^ 2, (d, E), dt, wl.w_std)
     w1 = normal(s ^ 3, (E, d, F), dt, wl.w_std)
     w_up = normal(s ^ 4, (E, d, F), dt, wl.w_std) if wl.act == "swiglu" else None
     w2 = normal(s ^ 5, (E, F, d), dt, wl.w_std)

@@ -1,0 +1,232 @@
+"""Helpers of the GPU parity tests: upload the seeded inputs, run one layer
+step through libmoe, download the results, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from mixture_experts_layer_36_amd.layer import MoELayer, Weights
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}     # max|err| / max|ref| per tensor
+TOL_LOGITS = 1e-5                      # fp32 accumulation in both dtypes
+
+
+def dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    """Device tensor -> numpy (floats widened exactly to float64)."""
+    if t is None:
+        return None
+    if t.dtype in (torch.bfloat16, torch.float32):
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def bits(t):
+    """Raw storage bits of a float tensor (for exact comparisons)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy()
+    return t.view(torch.int32).cpu().numpy()
+
+
+def storage_bits(a: np.ndarray):
+    return a.view(np.int16) if a.dtype == np.uint16 else a.view(np.int32)
+
+
+def make_layer(wl, inp):
+    layer = MoELayer(wl.T, wl.d, wl.ffn, wl.E, wl.k, wl.capacity_factor, wl.gating, wl.act,
+                     wl.dtype, wl.ep_ranks, wl.placement, wl.n_shared, wl.ffn_shared)
+    w = Weights(w_router=dev(inp.w_router), w1=dev(inp.w1), w2=dev(inp.w2), w_up=dev(inp.w_up),
+                bias=dev(inp.bias), ws_gate=dev(inp.ws_gate), ws_up=dev(inp.ws_up),
+                ws_down=dev(inp.ws_down))
+    return layer, w, dev(inp.x), dev(inp.dy)
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    if scale == 0.0:
+        return float(err)
+    return float(err / scale)
+
+
+def assert_close(name, got, ref, tol):
+    e = rel_err(got, ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def check_routing(wl, layer, ref, n_check_xperm_bits=True, x_bits=None):
+    """Bit-exact routing, layout and permutation against the oracle run on
+    the GPU's own fp32 logits."""
+    lay = ref["layout"]
+    T, k = wl.T, wl.k
+    np.testing.assert_array_equal(host(layer.topk_idx), ref["topk_idx"])
+    np.testing.assert_array_equal(host(layer.raw_counts), lay["raw_counts"])
+    np.testing.assert_array_equal(host(layer.expert_counts), lay["kept_counts"])
+    np.testing.assert_array_equal(host(layer.expert_offsets), lay["expert_offsets"])
+    np.testing.assert_array_equal(host(layer.send_counts), lay["send_counts"])
+    np.testing.assert_array_equal(host(layer.send_offsets), lay["send_offsets"])
+    np.testing.assert_array_equal(host(layer.row_of), lay["row_of"].reshape(T * k))
+    n = lay["n"]
+    np.testing.assert_array_equal(host(layer.assign_of_row)[:n], lay["assign_of_row"])
+    if x_bits is not None and n > 0:
+        xp = bits(layer.x_perm)[:n]
+        expect = x_bits[lay["assign_of_row"] // k]
+        np.testing.assert_array_equal(xp, expect)
+    return n
+
+
+def run_full_parity(wl, inp):
+    """Run one fwd+bwd step on the GPU and compare every output with the
+    oracle, element by element."""
+    layer, w, x, dy = make_layer(wl, inp)
+    layer.step(x, dy, w)
+    torch.cuda.synchronize()
+    g_logits = host(layer.logits)
+    ref = oracle.layer_from_inputs(inp, logits=g_logits)
+    tol = TOL[wl.dtype]
+    errs = {}
+    errs["logits"] = assert_close("logits", g_logits, ref["logits_ref"], TOL_LOGITS)
+    n = check_routing(wl, layer, ref, x_bits=storage_bits(inp.x))
+    errs["topk_w"] = assert_close("topk_w", host(layer.topk_w), ref["topk_w"], 1e-5)
+    errs["y"] = assert_close("y", host(layer.y), ref["y"], tol)
+    if n > 0:
+        errs["y_perm"] = assert_close("y_perm", host(layer.y_perm)[:n], ref["o_perm"], tol)
+    errs["d_topk_w"] = assert_close("d_topk_w", host(layer.d_topk_w), ref["d_topk_w"], tol)
+    errs["dlogits"] = assert_close("dlogits", host(layer.dlogits), ref["dlogits"], tol)
+    errs["dw_router"] = assert_close("dw_router", host(layer.dw_router), ref["dw_router"], tol)
+    errs["dw1"] = assert_close("dw1", host(layer.dw1), ref["dw1"], tol)
+    errs["dw2"] = assert_close("dw2", host(layer.dw2), ref["dw2"], tol)
+    if wl.act == "swiglu":
+        errs["dw_up"] = assert_close("dw_up", host(layer.dw_up), ref["dw_up"], tol)
+    if wl.n_shared:
+        errs["dws_gate"] = assert_close("dws_gate", host(layer.dws_gate), ref["dws_gate"], tol)
+        errs["dws_down"] = assert_close("dws_down", host(layer.dws_down), ref["dws_down"], tol)
+        if wl.act == "swiglu":
+            errs["dws_up"] = assert_close("dws_up", host(layer.dws_up), ref["dws_up"], tol)
+    errs["dx"] = assert_close("dx", host(layer.dx), ref["dx"], tol)
+    # experts with no rows get exact zeros
+    kept = ref["layout"]["kept_counts"]
+    for e in np.nonzero(kept == 0)[0]:
+        assert np.all(host(layer.dw1[e]) == 0.0) and np.all(host(layer.dw2[e]) == 0.0)
+    return layer, ref, errs
+
+
+def run_sampled_parity(wl, inp, n_tok=12, n_cols=6, seed=1):
+    """Full-size check: every integer output and the logits in full; float
+    outputs on sampled tokens (y, y_perm rows, d_topk_w, dlogits, dx) and
+    sampled hidden units of every expert's weight gradients, each computed
+    one by one by the oracle; dW_r through the identity dW_r = x^T dlogits
+    (holds at any size) with dlogits itself checked on the sample."""
+    layer, w, x, dy = make_layer(wl, inp)
+    layer.step(x, dy, w)
+    torch.cuda.synchronize()
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.ffn
+    tol = TOL[wl.dtype]
+    swiglu = wl.act == "swiglu"
+    X = oracle.to_f64(inp.x)
+    DY = oracle.to_f64(inp.dy)
+    Wr = oracle.to_f64(inp.w_router)
+    bias = None if inp.bias is None else oracle.to_f64(inp.bias)
+    g_logits = host(layer.logits)
+    assert_close("logits", g_logits, oracle.gate_logits(X, Wr, bias), TOL_LOGITS)
+    idx = oracle.select_topk(g_logits, k)
+    gw = oracle.gate_weights(g_logits, idx, wl.gating)
+    C = oracle.capacity(T, E, k, wl.capacity_factor)
+    lay = oracle.dispatch_layout(idx, E, C, wl.ep_ranks, wl.placement)
+    check_routing(wl, layer, dict(topk_idx=idx, layout=lay), x_bits=storage_bits(inp.x))
+    assert_close("topk_w", host(layer.topk_w), gw, 1e-5)
+
+    rng = np.random.default_rng(seed)
+    toks = sorted(set([0, T - 1] + [int(t) for t in rng.choice(T, n_tok, replace=False)]))
+    cols = sorted(set([0, F - 1] + [int(c) for c in rng.choice(F, n_cols, replace=False)]))
+    row_of = lay["row_of"].reshape(T, k)
+    ns = len(toks)
+    y_ref = np.zeros((ns, d))
+    dtw_ref = np.zeros((ns, k))
+    dx_ref = np.zeros((ns, d))
+    yp_got, yp_ref = [], []
+    cols_t = torch.tensor(cols, device=layer.dw1.device)
+    dw_got = {"dw1": [], "dw2": [], "dw_up": []}
+    dw_ref = {"dw1": [], "dw2": [], "dw_up": []}
+    off = lay["expert_offsets"]
+    slot_of = {int(e): s for s, e in enumerate(lay["slot_expert"])}
+    g_yperm = layer.y_perm
+    for e in range(E):
+        W1 = oracle.to_f64(inp.w1[e])
+        W2 = oracle.to_f64(inp.w2[e])
+        WU = oracle.to_f64(inp.w_up[e]) if swiglu else None
+        sel = [(i, j) for i, t in enumerate(toks) for j in range(k)
+               if idx[t, j] == e and row_of[t, j] >= 0]
+        if sel:
+            xs = X[[toks[i] for i, _ in sel]]
+            o = oracle.expert_ffn_forward(xs, W1, W2, wl.act, WU)["o"]
+            do = np.stack([gw[toks[i], j] * DY[toks[i]] for i, j in sel])
+            dxp = oracle.expert_ffn_backward(xs, do, W1, W2, wl.act, WU)["dxp"]
+            for r, (i, j) in enumerate(sel):
+                t = toks[i]
+                y_ref[i] += gw[t, j] * o[r]
+                dtw_ref[i, j] = DY[t] @ o[r]
+                dx_ref[i] += dxp[r]
+                yp_got.append(host(g_yperm[int(row_of[t, j])]))
+                yp_ref.append(o[r])
+        s = slot_of[e]
+        a = lay["assign_of_row"][off[s]:off[s + 1]]
+        tk, jj = a // k, a % k
+        xp_e = X[tk]
+        do_e = gw[tk, jj][:, None] * DY[tk]
+        b = oracle.expert_ffn_backward(xp_e, do_e, W1[:, cols], W2[cols, :], wl.act,
+                                       None if WU is None else WU[:, cols])
+        dw_got["dw1"].append(host(layer.dw1[e].index_select(1, cols_t)))
+        dw_ref["dw1"].append(b["dw_in"])
+        dw_got["dw2"].append(host(layer.dw2[e].index_select(0, cols_t)))
+        dw_ref["dw2"].append(b["dw_out"])
+        if swiglu:
+            dw_got["dw_up"].append(host(layer.dw_up[e].index_select(1, cols_t)))
+            dw_ref["dw_up"].append(b["dw_up"])
+    if wl.n_shared:
+        Fs = wl.ffn_shared
+        SG, SD = oracle.to_f64(inp.ws_gate), oracle.to_f64(inp.ws_down)
+        SU = oracle.to_f64(inp.ws_up) if swiglu else None
+        scols = sorted(set([0, wl.n_shared * Fs - 1] + [int(c) for c in rng.choice(wl.n_shared * Fs, n_cols, replace=False)]))
+        for sidx in range(wl.n_shared):
+            c = slice(sidx * Fs, (sidx + 1) * Fs)
+            f = oracle.expert_ffn_forward(X[toks], SG[:, c], SD[c, :], wl.act, None if SU is None else SU[:, c])
+            y_ref += f["o"]
+            dx_ref += oracle.expert_ffn_backward(X[toks], DY[toks], SG[:, c], SD[c, :], wl.act,
+                                                 None if SU is None else SU[:, c])["dxp"]
+        bs = oracle.expert_ffn_backward(X, DY, SG[:, scols], SD[scols, :], wl.act,
+                                        None if SU is None else SU[:, scols])
+        assert_close("dws_gate[cols]", host(layer.dws_gate)[:, scols], bs["dw_in"], tol)
+        assert_close("dws_down[cols]", host(layer.dws_down)[scols, :], bs["dw_out"], tol)
+        if swiglu:
+            assert_close("dws_up[cols]", host(layer.dws_up)[:, scols], bs["dw_up"], tol)
+    dl_ref = oracle.gating_backward(g_logits[toks], idx[toks], dtw_ref, wl.gating)
+    dx_ref += dl_ref @ Wr.T
+    errs = {}
+    errs["y"] = assert_close("y[tokens]", host(layer.y)[toks], y_ref, tol)
+    errs["y_perm"] = assert_close("y_perm[rows]", np.stack(yp_got), np.stack(yp_ref), tol)
+    errs["d_topk_w"] = assert_close("d_topk_w[tokens]", host(layer.d_topk_w)[toks], dtw_ref, tol)
+    g_dl = host(layer.dlogits)
+    errs["dlogits"] = assert_close("dlogits[tokens]", g_dl[toks], dl_ref, tol)
+    errs["dx"] = assert_close("dx[tokens]", host(layer.dx)[toks], dx_ref, tol)
+    for key in ("dw1", "dw2", "dw_up"):
+        if dw_got[key]:
+            errs[key] = assert_close(key + "[cols]", np.stack(dw_got[key]), np.stack(dw_ref[key]), tol)
+    errs["dw_router"] = assert_close("dw_router = x^T dlogits", host(layer.dw_router), X.T @ g_dl, tol)
+    np.testing.assert_allclose(g_dl.sum(axis=1), 0.0, atol=1e-4 * max(1.0, np.abs(g_dl).max()))
+    return layer, errs
