@@ -40,4 +40,11 @@ template <typename T>
 hipError_t run_wgrad(int epi, const Args& a, hipStream_t st);
 
 }  // namespace gemm
+
+// bf16 kernels with direct global -> LDS loads (gemm3.hip)
+namespace gemm3 {
+bool supports(const gemm::Args& a);
+hipError_t run_rows_bf16(int kind, int epi, const gemm::Args& a, int64_t rows_max, hipStream_t st);
+hipError_t run_wgrad_bf16(int epi, const gemm::Args& a, hipStream_t st);
+}  // namespace gemm3
 }  // namespace moe

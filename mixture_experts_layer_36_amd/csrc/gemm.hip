@@ -14,17 +14,23 @@
 //                       group's rows: ragged K; no rows -> exact zeros)
 // FWD and DGRAD split M (rows) by group; WGRAD splits K.
 //
-// Tiling.  A workgroup of 256 threads (4 waves, 2 x 2) computes a BM x BN
-// tile with v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32),
-// fp32 accumulation.  Each K stage moves 128 bytes of K per tile row (64 bf16
-// or 32 fp32) through LDS, double buffered with one barrier per stage; the
-// next stage's global loads are in flight while the current one is
-// multiplied.  LDS rows are K-contiguous (what an MFMA lane consumes: 16 bytes
-// of consecutive K) with an XOR swizzle of the 16-byte chunk index so that
-// both the fragment reads and the transposing writes spread over the banks.
+// Tiling.  A workgroup of WM x WN waves computes a BM x BN tile with
+// v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32), fp32
+// accumulation.  Each K stage moves 128 bytes of K per tile row (64 bf16 or
+// 32 fp32) through LDS, double buffered with one barrier per stage; the next
+// stage's global loads are in flight while the current one is multiplied,
+// and inside a stage the MFMA fragments of step s+1 are read from LDS while
+// step s multiplies.  LDS rows are K-contiguous (what an MFMA lane consumes:
+// 16 bytes of consecutive K) with an XOR swizzle of the 16-byte chunk index
+// so that fragment reads and transposing writes spread over the banks.
 // Operands whose global layout is M- or N-contiguous (forward weights,
 // wgrad activations) are loaded as 4(K) x 16-byte blocks and transposed in
 // registers on their way into LDS.
+//
+// Global loads are buffer loads: each operand gets a buffer resource based
+// at its tile (so offsets fit 32 bits) whose extent ends where the valid data
+// ends; a masked-off element is given an offset past the extent, which the
+// hardware range check turns into zeros.  No branches guard the loads.
 //
 // Tile order: hardware dispatches consecutive workgroups round-robin over
 // the 8 XCDs, each with its own L2; the linear tile id is remapped so that
@@ -33,17 +39,14 @@
 // activation panels in that XCD's L2.
 #include "common.h"
 #include "gemm.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace gemm {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+using namespace gemm_common;
 
-constexpr int NT = 256;
-constexpr int ROWB = 128;     // bytes of K per LDS row per stage
-constexpr int GM = 8;         // row-tiles per ordering group
-
+constexpr int ROWB = 128;                 // bytes of K per LDS row per stage
 __device__ __forceinline__ int swz(int row, int ch) {
   return ch ^ ((row ^ (row >> 3)) & 7);
 }
@@ -62,39 +65,6 @@ template <> struct Mma<float> {
       c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
   }
 };
-
-// Workgroup id -> linear tile id such that each XCD's workgroups get
-// consecutive tile ids (bijection on [0, num)).
-__device__ __forceinline__ int xcd_remap(int hw, int num) {
-  const int q = num >> 3, r = num & 7;
-  const int xcd = hw & 7, local = hw >> 3;
-  const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-  return base + local;
-}
-
-__device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt) {
-  const int span = GM * tiles_n;
-  const int gid = lin / span;
-  const int first = gid * GM;
-  const int gsz = min(tiles_m - first, GM);
-  const int rem = lin - gid * span;
-  mt = first + rem % gsz;
-  nt = rem / gsz;
-}
-
-__device__ __forceinline__ int weight_index(int g, int rr_R, int rr_L) {
-  // send slot g = q * L + l holds expert q + R * l under round-robin placement
-  return rr_R > 0 ? (g % rr_L) * rr_R + g / rr_L : g;
-}
-
-__device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-}
-__device__ __forceinline__ float gelu_grad_f(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
-         z * __expf(-0.5f * z * z) * 0.39894228040143268f;
-}
-__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
 // Transpose a 4(K) x V(MN) register block (4 x 16 bytes) into V rows of 4 K
 // elements and write them to LDS.
@@ -133,110 +103,173 @@ __device__ __forceinline__ void write_transposed<float>(char* lds, int row0, int
 }
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders.  A tile operand covers R rows (M or N) x 128 bytes of K.
-// K-contiguous source: R*8 16-byte chunks, R/32 per thread.
-// MN-contiguous source: 2R blocks of 4 K-rows x 16 bytes, R/128 per thread.
+// Operand tile loaders.  A tile operand covers R rows (M or N) x 128 bytes of
+// K per stage.  Per-thread byte offsets are computed once (voffset); the
+// stage's position along K travels in the scalar offset, and elements outside
+// the valid K range or columns get an offset past the resource extent.
 // ---------------------------------------------------------------------------
-template <typename T, int R>
-struct KLoader {
-  static constexpr int PER = R / 32;
-  u32x4 r[PER];
-  // src(row, k) returns a pointer or nullptr (-> zeros); k is an element index
-  template <typename Src>
-  __device__ __forceinline__ void load(const Src& src, int k0) {
-    constexpr int V = Vec16<T>::N;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + NT * i;
-      const int row = q >> 3, ch = q & 7;
-      const T* p = src(row, k0 + ch * V);
-      r[i] = p ? ld16(p) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + NT * i;
-      const int row = q >> 3, ch = q & 7;
-      *reinterpret_cast<u32x4*>(lds + row * ROWB + (swz(row, ch) << 4)) = r[i];
-    }
-  }
-};
-
-template <typename T, int R>
-struct MNLoader {
+// K-contiguous source (row r of the operand at r * ld elements from the
+// resource base): R*8 chunks of 16 bytes, chunk q -> (row q/8, chunk q%8).
+template <typename T, int R, int NTH>
+struct KLoad {
   static constexpr int V = Vec16<T>::N;
-  static constexpr int PER = R / 128;
-  static constexpr int NB = R / V;        // 16-byte blocks along MN per K row
-  u32x4 r[PER][4];
-  // src(k, mn) returns a pointer to 16 bytes (V elements along MN) or nullptr
-  template <typename Src>
-  __device__ __forceinline__ void load(const Src& src, int k0) {
+  static constexpr int PER = R * 8 / NTH;
+  static_assert(PER >= 1 && R * 8 % NTH == 0, "tile / thread mismatch");
+  u32x4 r[PER];
+  uint32_t voff[PER];
+  int kc;  // K offset of this thread's chunk within a stage
+
+  __device__ __forceinline__ void init(int64_t ld) {
+    kc = (threadIdx.x & 7) * V;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + NT * i;
-      const int kq = q / NB, nb = q % NB;
+      const int row = (i * NTH + (int)threadIdx.x) >> 3;
+      voff[i] = (uint32_t)(((int64_t)row * ld + kc) * (int64_t)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void load(const BufRes& b, int k0, int64_t K) {
+    const bool ok = k0 + kc < K;
+    const int soff = k0 * (int)sizeof(T);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const T* p = src(k0 + kq * 4 + kk, nb * V);
-        r[i][kk] = p ? ld16(p) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < PER; ++i)
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(b.r, ok ? voff[i] : kOOB, soff, 0);
+  }
+  // K split between two sources: k < split from b0 (at k), k >= split from
+  // b1 (at k - split).
+  __device__ __forceinline__ void load_split(const BufRes& b0, const BufRes& b1, int64_t ld, int k0, int64_t K,
+                                             int64_t split) {
+    constexpr int BKE = ROWB / sizeof(T);
+    if (k0 + BKE <= split) {
+      load(b0, k0, K);
+    } else if (k0 >= split) {
+      load(b1, k0 - (int)split, K - split);
+    } else {
+      const int64_t k = k0 + kc;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int row = (i * NTH + (int)threadIdx.x) >> 3;
+        const uint32_t o0 = (uint32_t)(((int64_t)row * ld + k) * (int64_t)sizeof(T));
+        const uint32_t o1 = (uint32_t)(((int64_t)row * ld + (k - split)) * (int64_t)sizeof(T));
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(b0.r, k < split ? o0 : kOOB, 0, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(b1.r, k >= split && k < K ? o1 : kOOB, 0, 0);
+        r[i] = v0 | v1;
       }
     }
   }
   __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + NT * i;
-      const int kq = q / NB, nb = q % NB;
-      write_transposed<T>(lds, nb * V, kq, r[i]);
+      const int q = i * NTH + threadIdx.x;
+      const int row = q >> 3, ch = q & 7;
+      *reinterpret_cast<u32x4*>(lds + row * ROWB + (swz(row, ch) << 4)) = r[i];
+    }
+  }
+};
+
+// MN-contiguous source (element (k, c) at k * ld + c elements from the base
+// of the resource of the half holding column c).  2R blocks of 4 K-rows x 16
+// bytes, numbered half-major so that every wave's load reads one half: the
+// two halves of the tile's columns may come from different tensors (the
+// paired gate / up weights of SwiGLU).
+template <typename T, int R, int NTH>
+struct MNLoad {
+  static constexpr int V = Vec16<T>::N;
+  static constexpr int PER = 2 * R / NTH;
+  static constexpr int RH = R / 2;
+  static constexpr int NBH = RH / V;       // 16-byte blocks along MN per K row and half
+  static_assert(PER >= 1 && 2 * R % NTH == 0 && R % 128 == 0, "tile / thread mismatch");
+  u32x4 r[PER][4];
+  uint32_t voff[PER];
+  int kq4[PER];     // first K row of the block within a stage
+  bool colok[PER];
+  int half[PER];    // wave-uniform
+
+  // col_base1: column of half 1 relative to its resource base; valid_cols:
+  // columns (relative to each resource base) that hold data.
+  __device__ __forceinline__ void init(int64_t ld, int col_base1, int64_t valid_cols) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = i * NTH + threadIdx.x;
+      half[i] = __builtin_amdgcn_readfirstlane(b / R);
+      const int rr = b % R;
+      kq4[i] = (rr / NBH) * 4;
+      const int c = (half[i] ? col_base1 : 0) + (rr % NBH) * V;
+      colok[i] = c < valid_cols;
+      voff[i] = (uint32_t)(((int64_t)kq4[i] * ld + c) * (int64_t)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void load(const BufRes& b0, const BufRes& b1, int64_t ld, int k0, int64_t Kvalid) {
+    const int row_bytes = (int)(ld * (int64_t)sizeof(T));
+    const int soff = k0 * row_bytes;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const BufRes& br = half[i] ? b1 : b0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bool ok = colok[i] && (k0 + kq4[i] + kk < Kvalid);
+        r[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(br.r, ok ? voff[i] + kk * row_bytes : kOOB, soff, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = i * NTH + threadIdx.x;
+      const int h = b / R, rr = b % R;
+      write_transposed<T>(lds, h * RH + (rr % NBH) * V, rr / NBH, r[i]);
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// MFMA over one LDS stage for a wave's (BM/2) x (BN/2) sub-tile.
+// MFMA over one LDS stage for a wave's FM x FN blocks of 32 x 32; fragments of
+// k-step s+1 are read while k-step s multiplies.
 // ---------------------------------------------------------------------------
 template <typename T, int FM, int FN>
 __device__ __forceinline__ void mma_stage(const char* la, const char* lb, int wm0, const int (&bcol)[FN],
                                           f32x16 (&acc)[FM][FN]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  u32x4 af[2][FM], bfr[2][FN];
+  auto fetch = [&](int s, int buf) {
     const int ch = 2 * s + g;
-    u32x4 af[FM], bfr[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm0 + i * 32 + r;
-      af[i] = *reinterpret_cast<const u32x4*>(la + row * ROWB + (swz(row, ch) << 4));
+      af[buf][i] = *reinterpret_cast<const u32x4*>(la + row * ROWB + (swz(row, ch) << 4));
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = bcol[j] + r;
-      bfr[j] = *reinterpret_cast<const u32x4*>(lb + row * ROWB + (swz(row, ch) << 4));
+      bfr[buf][j] = *reinterpret_cast<const u32x4*>(lb + row * ROWB + (swz(row, ch) << 4));
     }
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    // keep the reads of step s+1 ahead of the MFMAs of step s
+    if (s < 3) fetch(s + 1, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+      for (int j = 0; j < FN; ++j) Mma<T>::run(acc[i][j], af[s & 1][i], bfr[s & 1][j]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-}
-
-// Row of accumulator element e (0..15) of a 32x32 block for this lane.
-__device__ __forceinline__ int acc_row(int e, int lane) {
-  return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
 }
 
 // ---------------------------------------------------------------------------
 // FWD / DGRAD: rows split by group.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int KIND, int EPI>
-__global__ __launch_bounds__(NT) void gemm_rows_kernel(Args a) {
-  constexpr int FM = BM / 64, FN = BN / 64;
-  constexpr int V = Vec16<T>::N;
+template <typename T, int BM, int BN, int WM, int WN, int PIPE, int KIND, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_rows_kernel(Args a) {
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr int BKE = ROWB / sizeof(T);
-  constexpr bool SWIGLU_PAIR = (EPI == EPI_SWIGLU_FWD);
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
+  constexpr int S = sizeof(T);
+  constexpr bool PAIR = (EPI == EPI_SWIGLU_FWD);
+  static_assert(!PAIR || FN % 2 == 0, "SwiGLU pairing needs an even number of N-blocks per wave");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   int mt, nt;
@@ -261,56 +294,55 @@ __global__ __launch_bounds__(NT) void gemm_rows_kernel(Args a) {
   }
   if (g < 0) return;
   const int wi = weight_index(g, a.rr_R, a.rr_L);
-  const int64_t K = a.K;
-  const int64_t N = a.N;
+  const int64_t K = a.K, N = a.N;
+  const int64_t rows_valid = min((int64_t)BM, row_end - row_begin);
+  const int64_t n0 = PAIR ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
 
-  const T* Ab = reinterpret_cast<const T*>(a.A);
-  const T* Bg = reinterpret_cast<const T*>(a.B) + (int64_t)wi * a.b_gstride;
-  const T* B2g = a.B2 ? reinterpret_cast<const T*>(a.B2) + (int64_t)wi * a.b_gstride : nullptr;
+  const char* Ab = reinterpret_cast<const char*>(a.A);
+  const char* Bg = reinterpret_cast<const char*>(a.B) + (int64_t)wi * a.b_gstride * S;
+  const char* B2g = a.B2 ? reinterpret_cast<const char*>(a.B2) + (int64_t)wi * a.b_gstride * S : Bg;
 
-  // tile column c -> weight column (and which weight for the SwiGLU pairing)
-  const int64_t n0 = SWIGLU_PAIR ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
+  BufRes ra, rb0, rb1;
+  ra.init(Ab + row_begin * a.lda * S, rows_valid * a.lda * S);
+  if (KIND == KIND_FWD) {
+    rb0.init(Bg + n0 * S, K * a.ldb * S - n0 * S);
+    rb1.init(B2g + n0 * S, K * a.ldb * S - n0 * S);
+  } else {
+    rb0.init(Bg + n0 * a.ldb * S, (N - n0) * a.ldb * S);
+    rb1.init(B2g + n0 * a.ldb * S, (N - n0) * a.ldb * S);
+  }
+  const int col_base1 = PAIR ? 0 : BN / 2;
+  const int64_t valid_cols = N - n0;
 
-  auto a_src = [&](int row, int k) -> const T* {
-    const int64_t rr = row_begin + row;
-    if (rr >= row_end || k >= K) return nullptr;
-    return Ab + rr * a.lda + k;
-  };
-
-  KLoader<T, BM> la_ld;
-  KLoader<T, BN> lbk_ld;   // DGRAD: weights K-contiguous
-  MNLoader<T, BN> lbn_ld;  // FWD: weights N-contiguous
-
-  auto b_src_n = [&](int k, int c) -> const T* {   // FWD: element (k, tile col c..c+V)
-    if (k >= K) return nullptr;
-    if (SWIGLU_PAIR) {
-      const int half = c >= BN / 2;
-      const int64_t f = n0 + (half ? c - BN / 2 : c);
-      if (f >= N) return nullptr;
-      return (half ? B2g : Bg) + (int64_t)k * a.ldb + f;
-    }
-    const int64_t n = n0 + c;
-    if (n >= N) return nullptr;
-    return Bg + (int64_t)k * a.ldb + n;
-  };
-  auto b_src_k = [&](int c, int k) -> const T* {   // DGRAD: element (tile col c, k..k+V)
-    const int64_t n = n0 + c;
-    if (n >= N || k >= K) return nullptr;
-    if (a.b_split > 0 && k >= a.b_split) return B2g + n * a.ldb + (k - a.b_split);
-    return Bg + n * a.ldb + k;
+  // PIPE register sets of staged global loads: the loads of stage kt+PIPE
+  // are issued as soon as stage kt has been written to LDS, so every load has
+  // PIPE stages of MFMA work to arrive.
+  KLoad<T, BM, NTH> la0, la1;
+  KLoad<T, BN, NTH> lbk0, lbk1;   // DGRAD: weights K-contiguous
+  MNLoad<T, BN, NTH> lbn0, lbn1;  // FWD: weights N-contiguous
+  la0.init(a.lda);
+  la1.init(a.lda);
+  if (KIND == KIND_FWD) {
+    lbn0.init(a.ldb, col_base1, valid_cols);
+    lbn1.init(a.ldb, col_base1, valid_cols);
+  } else {
+    lbk0.init(a.ldb);
+    lbk1.init(a.ldb);
+  }
+  auto load_stage = [&](auto& la, auto& lbk, auto& lbn, int k0) {
+    la.load(ra, k0, K);
+    if (KIND == KIND_FWD)
+      lbn.load(rb0, rb1, a.ldb, k0, K);
+    else if (a.b_split > 0)
+      lbk.load_split(rb0, rb1, a.ldb, k0, K, a.b_split);
+    else
+      lbk.load(rb0, k0, K);
   };
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm0 = (wave >> 1) * (BM / 2);
-  const int wn = wave & 1;
+  const int wm0 = (wave / WN) * (BM / WM);
   int bcol[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    if (SWIGLU_PAIR)
-      bcol[j] = j < FN / 2 ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - FN / 2) * 32;
-    else
-      bcol[j] = wn * (BN / 2) + j * 32;
-  }
+  block_cols<BN, WN, FN, PAIR>(wave % WN, bcol);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -321,74 +353,27 @@ __global__ __launch_bounds__(NT) void gemm_rows_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((K + BKE - 1) / BKE);
-  la_ld.load(a_src, 0);
-  if (KIND == KIND_FWD) lbn_ld.load(b_src_n, 0); else lbk_ld.load(b_src_k, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](auto& la, auto& lbk, auto& lbn, int kt) {
     char* sa = smem + (kt & 1) * (BM + BN) * ROWB;
     char* sb = sa + BM * ROWB;
-    la_ld.store(sa);
-    if (KIND == KIND_FWD) lbn_ld.store(sb); else lbk_ld.store(sb);
+    la.store(sa);
+    if (KIND == KIND_FWD) lbn.store(sb); else lbk.store(sb);
     __syncthreads();
-    if (kt + 1 < nk) {
-      const int k0 = (kt + 1) * BKE;
-      la_ld.load(a_src, k0);
-      if (KIND == KIND_FWD) lbn_ld.load(b_src_n, k0); else lbk_ld.load(b_src_k, k0);
-    }
+    if (kt + PIPE < nk) load_stage(la, lbk, lbn, (kt + PIPE) * BKE);
     mma_stage<T, FM, FN>(sa, sb, wm0, bcol, acc);
+  };
+  if (nk > 0) load_stage(la0, lbk0, lbn0, 0);
+  if constexpr (PIPE == 1) {
+    for (int kt = 0; kt < nk; ++kt) step(la0, lbk0, lbn0, kt);
+  } else {
+    if (nk > 1) load_stage(la1, lbk1, lbn1, BKE);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(la0, lbk0, lbn0, kt);
+      if (kt + 1 < nk) step(la1, lbk1, lbn1, kt + 1);
+    }
   }
 
-  // ---------------------------------------------------------------- epilogue
-  T* C = reinterpret_cast<T*>(a.C);
-  T* C2 = reinterpret_cast<T*>(a.C2);
-  const T* X1 = reinterpret_cast<const T*>(a.X1);
-  const int col = lane & 31;
-  if constexpr (SWIGLU_PAIR) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j) {
-        const int64_t f = n0 + bcol[j] + col;
-        if (f >= N) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t rr = row_begin + wm0 + i * 32 + acc_row(e, lane);
-          if (rr >= row_end) continue;
-          const float av = acc[i][j][e], bv = acc[i][j + FN / 2][e];
-          C[rr * a.ldc + f] = from_f32<T>(av);
-          C[rr * a.ldc + a.c_split + f] = from_f32<T>(bv);
-          C2[rr * a.ldc2 + f] = from_f32<T>(av * sigmoid_f(av) * bv);
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t n = n0 + bcol[j] + col;
-        if (n >= N) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t rr = row_begin + wm0 + i * 32 + acc_row(e, lane);
-          if (rr >= row_end) continue;
-          const float v = acc[i][j][e];
-          if constexpr (EPI == EPI_STORE) {
-            C[rr * a.ldc + n] = from_f32<T>(v);
-          } else if constexpr (EPI == EPI_GELU_FWD) {
-            C[rr * a.ldc + n] = from_f32<T>(v);
-            C2[rr * a.ldc2 + n] = from_f32<T>(gelu_f(v));
-          } else if constexpr (EPI == EPI_GELU_BWD) {
-            const float z = to_f32(X1[rr * a.ldx + n]);
-            C[rr * a.ldc + n] = from_f32<T>(v * gelu_grad_f(z));
-          } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            const float av = to_f32(X1[rr * a.ldx + n]);
-            const float bv = to_f32(X1[rr * a.ldx + a.c_split + n]);
-            const float s = sigmoid_f(av);
-            C[rr * a.ldc + n] = from_f32<T>(v * bv * s * (1.0f + av * (1.0f - s)));
-            C[rr * a.ldc + a.c_split + n] = from_f32<T>(v * av * s);
-          }
-        }
-      }
-  }
+  rows_epilogue<T, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -396,11 +381,13 @@ __global__ __launch_bounds__(NT) void gemm_rows_kernel(Args a) {
 // MN-contiguous in memory.  EPI_STORE or EPI_STORE_SPLITN (columns >= c_split
 // go to C2 at column - c_split).
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int EPI>
-__global__ __launch_bounds__(NT) void gemm_wgrad_kernel(Args a) {
-  constexpr int FM = BM / 64, FN = BN / 64;
+template <typename T, int BM, int BN, int WM, int WN, int PIPE, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_wgrad_kernel(Args a) {
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr int BKE = ROWB / sizeof(T);
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
+  constexpr int S = sizeof(T);
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = a.tiles_m * a.tiles_n;
@@ -414,25 +401,22 @@ __global__ __launch_bounds__(NT) void gemm_wgrad_kernel(Args a) {
   const int64_t M = a.M, N = a.N;
   const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
 
-  const T* X = reinterpret_cast<const T*>(a.A);
-  const T* D = reinterpret_cast<const T*>(a.B);
-  auto a_src = [&](int k, int m) -> const T* {
-    if (k >= Kr || m0 + m >= M) return nullptr;
-    return X + (r0 + k) * a.lda + m0 + m;
-  };
-  auto b_src = [&](int k, int n) -> const T* {
-    if (k >= Kr || n0 + n >= N) return nullptr;
-    return D + (r0 + k) * a.ldb + n0 + n;
-  };
-  MNLoader<T, BM> la_ld;
-  MNLoader<T, BN> lb_ld;
+  const char* X = reinterpret_cast<const char*>(a.A);
+  const char* D = reinterpret_cast<const char*>(a.B);
+  BufRes ra, rb;
+  ra.init(X + (r0 * a.lda + m0) * S, Kr * a.lda * S - m0 * S);
+  rb.init(D + (r0 * a.ldb + n0) * S, Kr * a.ldb * S - n0 * S);
+  MNLoad<T, BM, NTH> la0, la1;
+  MNLoad<T, BN, NTH> lb0, lb1;
+  la0.init(a.lda, BM / 2, M - m0);
+  la1.init(a.lda, BM / 2, M - m0);
+  lb0.init(a.ldb, BN / 2, N - n0);
+  lb1.init(a.ldb, BN / 2, N - n0);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm0 = (wave >> 1) * (BM / 2);
-  const int wn = wave & 1;
+  const int wm0 = (wave / WN) * (BM / WM);
   int bcol[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) bcol[j] = wn * (BN / 2) + j * 32;
+  block_cols<BN, WN, FN, false>(wave % WN, bcol);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -443,49 +427,37 @@ __global__ __launch_bounds__(NT) void gemm_wgrad_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((Kr + BKE - 1) / BKE);
-  if (nk > 0) {
-    la_ld.load(a_src, 0);
-    lb_ld.load(b_src, 0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
+  auto load_stage = [&](auto& la, auto& lb, int k0) {
+    la.load(ra, ra, a.lda, k0, Kr);
+    lb.load(rb, rb, a.ldb, k0, Kr);
+  };
+  auto step = [&](auto& la, auto& lb, int kt) {
     char* sa = smem + (kt & 1) * (BM + BN) * ROWB;
     char* sb = sa + BM * ROWB;
-    la_ld.store(sa);
-    lb_ld.store(sb);
+    la.store(sa);
+    lb.store(sb);
     __syncthreads();
-    if (kt + 1 < nk) {
-      la_ld.load(a_src, (kt + 1) * BKE);
-      lb_ld.load(b_src, (kt + 1) * BKE);
-    }
+    if (kt + PIPE < nk) load_stage(la, lb, (kt + PIPE) * BKE);
     mma_stage<T, FM, FN>(sa, sb, wm0, bcol, acc);
+  };
+  if (nk > 0) load_stage(la0, lb0, 0);
+  if constexpr (PIPE == 1) {
+    for (int kt = 0; kt < nk; ++kt) step(la0, lb0, kt);
+  } else {
+    if (nk > 1) load_stage(la1, lb1, BKE);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(la0, lb0, kt);
+      if (kt + 1 < nk) step(la1, lb1, kt + 1);
+    }
   }
 
-  T* C = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride;
-  T* C2 = a.C2 ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride : nullptr;
-  const int col = lane & 31;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + bcol[j] + col;
-      if (n >= N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm0 + i * 32 + acc_row(e, lane);
-        if (m >= M) continue;
-        const T v = from_f32<T>(acc[i][j][e]);
-        if (EPI == EPI_STORE_SPLITN && n >= a.c_split)
-          C2[m * a.ldc + (n - a.c_split)] = v;
-        else
-          C[m * a.ldc + n] = v;
-      }
-    }
+  wgrad_epilogue<T, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int KIND, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int PIPE, int KIND, int EPI>
 static hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   const int tiles_n_cols = EPI == EPI_SWIGLU_FWD ? BN / 2 : BN;
   a.tiles_n = (int)((a.N + tiles_n_cols - 1) / tiles_n_cols);
@@ -493,35 +465,49 @@ static hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_rows_kernel<T, BM, BN, KIND, EPI>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+  const size_t lds = 2 * (BM + BN) * ROWB;
+  auto kern = gemm_rows_kernel<T, BM, BN, WM, WN, PIPE, KIND, EPI>;
+  static hipError_t prep = prepare_lds(kern, lds);
+  if (prep != hipSuccess) return prep;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int PIPE, int EPI>
 static hipError_t launch_wgrad(Args a, hipStream_t st) {
   a.tiles_m = (int)((a.M + BM - 1) / BM);
   a.tiles_n = (int)((a.N + BN - 1) / BN);
   const int64_t grid = (int64_t)a.groups * a.tiles_m * a.tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_wgrad_kernel<T, BM, BN, EPI>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+  const size_t lds = 2 * (BM + BN) * ROWB;
+  auto kern = gemm_wgrad_kernel<T, BM, BN, WM, WN, PIPE, EPI>;
+  static hipError_t prep = prepare_lds(kern, lds);
+  if (prep != hipSuccess) return prep;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
   return hipGetLastError();
 }
 
+#ifndef MOE_GEMM_CFG
+#define MOE_GEMM_CFG 128, 128, 2, 2, 1
+#endif
+
 template <typename T>
 hipError_t run_rows(int kind, int epi, const Args& a, int64_t rows_max, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
+  if constexpr (sizeof(T) == 2) {
+    if (gemm3::supports(a)) return gemm3::run_rows_bf16(kind, epi, a, rows_max, st);
+  }
   if (kind == KIND_FWD) {
     switch (epi) {
-      case EPI_STORE: return launch_rows<T, BM, BN, KIND_FWD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_FWD: return launch_rows<T, BM, BN, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
-      case EPI_SWIGLU_FWD: return launch_rows<T, BM, BN, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
+      case EPI_STORE: return launch_rows<T, MOE_GEMM_CFG, KIND_FWD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_FWD: return launch_rows<T, MOE_GEMM_CFG, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
+      case EPI_SWIGLU_FWD: return launch_rows<T, MOE_GEMM_CFG, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
     }
   } else {
     switch (epi) {
-      case EPI_STORE: return launch_rows<T, BM, BN, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_BWD: return launch_rows<T, BM, BN, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
-      case EPI_SWIGLU_BWD: return launch_rows<T, BM, BN, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+      case EPI_STORE: return launch_rows<T, MOE_GEMM_CFG, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_BWD: return launch_rows<T, MOE_GEMM_CFG, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<T, MOE_GEMM_CFG, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   }
   return hipErrorInvalidValue;
@@ -529,9 +515,11 @@ hipError_t run_rows(int kind, int epi, const Args& a, int64_t rows_max, hipStrea
 
 template <typename T>
 hipError_t run_wgrad(int epi, const Args& a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
-  if (epi == EPI_STORE) return launch_wgrad<T, BM, BN, EPI_STORE>(a, st);
-  if (epi == EPI_STORE_SPLITN) return launch_wgrad<T, BM, BN, EPI_STORE_SPLITN>(a, st);
+  if constexpr (sizeof(T) == 2) {
+    if (gemm3::supports(a)) return gemm3::run_wgrad_bf16(epi, a, st);
+  }
+  if (epi == EPI_STORE) return launch_wgrad<T, MOE_GEMM_CFG, EPI_STORE>(a, st);
+  if (epi == EPI_STORE_SPLITN) return launch_wgrad<T, MOE_GEMM_CFG, EPI_STORE_SPLITN>(a, st);
   return hipErrorInvalidValue;
 }
 

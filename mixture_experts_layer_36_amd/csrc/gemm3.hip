@@ -1,0 +1,506 @@
+// bf16 grouped expert GEMMs with direct global -> LDS loads (gfx950).
+//
+// Same three launch kinds and epilogues as the register-staged kernels of
+// gemm.hip (FWD, DGRAD split rows by group; WGRAD splits the reduction by
+// group), built around two gfx950 features:
+//
+//  * buffer_load_dwordx4 ... lds: every lane's 16 bytes go straight from
+//    global memory into LDS at M0 + 16 * lane, without passing through
+//    registers.  The loads of a K stage therefore cost no VGPRs, and the
+//    tile ring holds NS stages in flight (NS - 1 stages of loads overlap the
+//    MFMA work of the current one).  A lane's global address is chosen so
+//    that its 16 bytes land in the XOR-swizzled slot the fragment reads
+//    expect; masked-off lanes get an offset past the buffer extent and the
+//    hardware range check writes zeros.
+//  * ds_read_b64_tr_b16: operands whose global layout is M- or N-contiguous
+//    (forward weights, both wgrad operands) are kept in LDS in that layout,
+//    as panels of [K][128 columns]; within each 16-lane group the transposing
+//    read hands lane i the 4 consecutive K values of column i of a 4 x 16
+//    block, so two reads build the 8-element K run an MFMA lane consumes.
+//    K-contiguous operands (the activation rows of FWD / DGRAD, the weights
+//    of DGRAD) are stored [rows][BK] and read with ds_read_b128.
+//
+// Synchronisation per stage: wait until this wave's loads of the stage have
+// landed (vmcnt), barrier (all waves' loads landed and all waves finished the
+// previous stage), issue the loads of stage kt + NS - 1 into the slot the
+// previous stage used, multiply the current stage.
+//
+// Workgroup: WM x WN waves, tile BM x BN, MFMA v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation.  Tile order as in gemm.hip (XCD-aware, grouped rows).
+#include "common.h"
+#include "gemm.h"
+#include "gemm_common.h"
+
+namespace moe {
+namespace gemm3 {
+
+using gemm::Args;
+using namespace gemm_common;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  // n is wave-uniform and small; dispatch to immediates
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 32: wait_vmcnt<32>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void lds_load16(const BufRes& b, char* lds_unit, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_unit, 16, voff, soff, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Layout of one stage of an operand in LDS.
+//   K-contiguous (KC): [R rows][BK], row pitch BK*2 bytes, 16-byte chunk c of
+//     row r stored at chunk c ^ kc_swz(r).
+//   MN-contiguous: panels of 128 columns, each [BK][128], pitch 256 bytes,
+//     chunk c of K-row k stored at chunk c ^ (4 * (k & 3)).
+// ---------------------------------------------------------------------------
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row) {
+  if constexpr (BK == 32) return (row >> 2) & 3;
+  else return (row ^ (row >> 3)) & 7;
+}
+__device__ __forceinline__ int mn_swz(int k) { return 4 * (k & 3); }
+
+// One operand's direct loads.  The stage is split into 1 KiB units; unit u of
+// the stage is issued by wave u % NW as its (u / NW)-th load.
+template <int R, int BK, bool KC, int NW>
+struct Loader {
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int UNITS = BYTES / 1024;
+  static_assert(UNITS % NW == 0, "units must split evenly over the waves");
+  static constexpr int PER = UNITS / NW;
+  uint32_t voff[PER];
+  int krow[PER];      // MN: K row (within the stage) this lane loads
+  bool colok[PER];    // MN: column in range
+  int kcol[PER];      // KC: K element offset (within the stage) of this lane's chunk
+
+  // KC: source row r of the operand is at r * ld elements from the base.
+  __device__ __forceinline__ void init_kc(int64_t ld) {
+    constexpr int CPR = BK * 2 / 16;     // chunks per row
+    constexpr int RPU = 64 / CPR;        // rows per unit
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = i * NW + wave;
+      const int row = u * RPU + lane / CPR;
+      const int c = p ^ kc_swz<BK>(row);
+      kcol[i] = c * 8;
+      voff[i] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+      krow[i] = 0;
+      colok[i] = true;
+    }
+  }
+  // MN: element (k, col) at k * ld + col elements from the base of the
+  // resource of the column's panel (col relative to that base).
+  __device__ __forceinline__ void init_mn(int64_t ld, bool pair, int64_t valid_cols) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int KB = BK / 4;  // units per panel (4 K rows each)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = i * NW + wave;
+      const int panel = u / KB;
+      const int k = (u % KB) * 4 + lane / 16;
+      const int c = (lane % 16) ^ mn_swz(k);
+      const int col = (pair ? 0 : panel * 128) + c * 8;
+      krow[i] = k;
+      colok[i] = col < valid_cols;
+      voff[i] = (uint32_t)(((int64_t)k * ld + col) * 2);
+    }
+  }
+  // Issue the loads of a stage.  KC: K range [k0, K); MN: K rows [k0, Kvalid).
+  template <typename ResOf>
+  __device__ __forceinline__ void issue(char* stage, const ResOf& res_of_panel, int k0, int64_t Klim,
+                                        int64_t ld) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = i * NW + wave;
+      char* dst = stage + u * 1024;
+      if constexpr (KC) {
+        const bool ok = k0 + kcol[i] < Klim;
+        lds_load16(res_of_panel(0), dst, ok ? voff[i] : kOOB, (uint32_t)(k0 * 2));
+      } else {
+        constexpr int KB = BK / 4;
+        const int panel = u / KB;
+        const bool ok = colok[i] && (k0 + krow[i] < Klim);
+        lds_load16(res_of_panel(panel), dst, ok ? voff[i] : kOOB, (uint32_t)((int64_t)k0 * ld * 2));
+      }
+    }
+  }
+};
+
+// Fragment reads are issued as inline asm: the compiler cannot tell that they
+// never touch an LDS slot with loads in flight and would otherwise wait for
+// every outstanding global->LDS load before each read.  Their completion is
+// tracked by hand with lgkmcnt (LDS reads complete in order; the loop issues
+// no scalar memory loads).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  // vmcnt = 63 (bits [3:0] = 15, [15:14] = 3), expcnt = 7
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
+// K-contiguous fragment: 8 consecutive K of row `row` at k-step s.
+template <int BK>
+__device__ __forceinline__ u32x4 frag_kc(uint32_t tile, int row, int s, int g) {
+  const int ch = 2 * s + g;
+  return ds_read_b128(tile + row * (BK * 2) + ((ch ^ kc_swz<BK>(row)) << 4));
+}
+
+// MN-contiguous fragment of the 32-column block starting at tile column n0:
+// lane l gets K = 16 s + 8 (l / 32) + 0..7 of column n0 + (l % 32).
+template <int BK>
+__device__ __forceinline__ u32x4 frag_mn(uint32_t tile, int n0, int s, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int n = n0 + (G & 1) * 16 + 4 * (j & 3);
+  const int panel = n >> 7, nc = n & 127;
+  const uint32_t pbase = tile + panel * (BK * 256);
+  u32x4 out;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = 16 * s + (G >> 1) * 8 + 4 * r + (j >> 2);
+    const u32x2 w = ds_read_tr16(pbase + k * 256 + (((nc >> 3) ^ mn_swz(k)) << 4) + (nc & 7) * 2);
+    out[2 * r] = w[0];
+    out[2 * r + 1] = w[1];
+  }
+  return out;
+}
+
+template <bool KC, int BK>
+__device__ __forceinline__ u32x4 frag(uint32_t tile, int row, int s, int lane) {
+  if constexpr (KC) return frag_kc<BK>(tile, row + (lane & 31), s, lane >> 5);
+  else return frag_mn<BK>(tile, row, s, lane);
+}
+
+// MFMA over one stage (BK / 16 k-steps), fragments of step s+1 read while step
+// s multiplies.
+template <int FM, int FN, int BK, bool AKC, bool BKC>
+__device__ __forceinline__ void mma_stage(const char* ta_p, const char* tb_p, int wm0, const int (&bcol)[FN],
+                                          f32x16 (&acc)[FM][FN]) {
+  constexpr int STEPS = BK / 16;
+  constexpr int READS = FM * (AKC ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS reads per step
+  const uint32_t ta = lds_addr(ta_p), tb = lds_addr(tb_p);
+  const int lane = threadIdx.x & 63;
+  u32x4 af[2][FM], bfr[2][FN];
+  auto fetch = [&](int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[buf][i] = frag<AKC, BK>(ta, wm0 + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[buf][j] = frag<BKC, BK>(tb, bcol[j], s, lane);
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    // keep the reads of step s+1 ahead of the MFMAs of step s
+    if (s + 1 < STEPS) {
+      fetch(s + 1, (s + 1) & 1);
+      wait_lgkmcnt<(READS < 15 ? READS : 15)>();  // conservative when the count saturates
+    } else {
+      wait_lgkmcnt<0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[s & 1][i]),
+                                                            __builtin_bit_cast(bf16x8, bfr[s & 1][j]),
+                                                            acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The pipelined K loop shared by both kernels.
+template <int NS, int STAGE_BYTES, typename Issue, typename Compute>
+__device__ __forceinline__ void k_loop(char* smem, int nk, int loads_per_stage, const Issue& issue,
+                                       const Compute& compute) {
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(smem + s * STAGE_BYTES, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(NS - 2, nk - 1 - kt);
+    wait_vmcnt_dyn(ahead * loads_per_stage);
+    barrier();
+    if (kt + NS - 1 < nk) issue(smem + ((kt + NS - 1) % NS) * STAGE_BYTES, kt + NS - 1);
+    compute(smem + (kt % NS) * STAGE_BYTES);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FWD / DGRAD: rows split by group.  A = activation rows (K-contiguous).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int BK, int NS, int KIND, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
+  constexpr bool PAIR = (EPI == gemm::EPI_SWIGLU_FWD);
+  constexpr bool BKC = (KIND == gemm::KIND_DGRAD);
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  static_assert(!PAIR || BN == 256, "gate/up pairing puts one 128-column panel per half");
+  static_assert(BM % 128 == 0 && BN % 128 == 0 && (BK == 32 || BK == 64), "tile shape");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  int mt, nt;
+  grouped_order(lin, a.tiles_m, a.tiles_n, mt, nt);
+  if (mt >= a.tiles_m) return;
+  int g = -1;
+  int64_t row_begin = 0, row_end = 0;
+  {
+    int acc_t = 0;
+    for (int gg = 0; gg < a.groups; ++gg) {
+      const int64_t o0 = a.offsets[gg], o1 = a.offsets[gg + 1];
+      const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
+      if (mt < acc_t + nt_g) {
+        g = gg;
+        row_begin = o0 + (int64_t)(mt - acc_t) * BM;
+        row_end = o1;
+        break;
+      }
+      acc_t += nt_g;
+    }
+  }
+  if (g < 0) return;
+  const int wi = weight_index(g, a.rr_R, a.rr_L);
+  const int64_t K = a.K, N = a.N;
+  const int64_t rows_valid = min((int64_t)BM, row_end - row_begin);
+  const int64_t n0 = PAIR ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
+
+  const char* Ab = reinterpret_cast<const char*>(a.A);
+  const char* Bg = reinterpret_cast<const char*>(a.B) + (int64_t)wi * a.b_gstride * 2;
+  const char* B2g = a.B2 ? reinterpret_cast<const char*>(a.B2) + (int64_t)wi * a.b_gstride * 2 : Bg;
+
+  BufRes ra, rb0, rb1;
+  ra.init(Ab + row_begin * a.lda * 2, rows_valid * a.lda * 2);
+  if (KIND == gemm::KIND_FWD) {
+    rb0.init(Bg + n0 * 2, K * a.ldb * 2 - n0 * 2);
+    rb1.init(B2g + n0 * 2, K * a.ldb * 2 - n0 * 2);
+  } else {
+    rb0.init(Bg + n0 * a.ldb * 2, (N - n0) * a.ldb * 2);
+    rb1.init(B2g + n0 * a.ldb * 2, (N - n0) * a.ldb * 2);
+  }
+
+  Loader<BM, BK, true, NW> la;
+  Loader<BN, BK, BKC, NW> lb;
+  la.init_kc(a.lda);
+  if constexpr (BKC) lb.init_kc(a.ldb);
+  else lb.init_mn(a.ldb, PAIR, N - n0);
+  const bool split = BKC && a.b_split > 0;
+
+  auto issue = [&](char* stage, int kt) {
+    const int k0 = kt * BK;
+    la.issue(stage, [&](int) -> const BufRes& { return ra; }, k0, K, a.lda);
+    if constexpr (BKC) {
+      if (split && k0 >= a.b_split)
+        lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb1; }, k0 - (int)a.b_split, K - a.b_split,
+                 a.ldb);
+      else
+        lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb0; }, k0, split ? a.b_split : K, a.ldb);
+    } else {
+      lb.issue(stage + A_BYTES, [&](int p) -> const BufRes& { return (PAIR && p) ? rb1 : rb0; }, k0, K, a.ldb);
+    }
+  };
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm0 = (wave / WN) * (BM / WM);
+  int bcol[FN];
+  block_cols<BN, WN, FN, PAIR>(wave % WN, bcol);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = (int)((K + BK - 1) / BK);
+  k_loop<NS, STAGE>(smem, nk, Loader<BM, BK, true, NW>::PER + Loader<BN, BK, BKC, NW>::PER, issue,
+                    [&](const char* st) { mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc); });
+
+  rows_epilogue<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
+}
+
+// ---------------------------------------------------------------------------
+// WGRAD: C_g[M, N] = X[rows_g, M]^T . D[rows_g, N], both MN-contiguous.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_g = a.tiles_m * a.tiles_n;
+  const int g = lin / per_g;
+  if (g >= a.groups) return;
+  int mt, nt;
+  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt);
+  const int wi = weight_index(g, a.rr_R, a.rr_L);
+  const int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
+  const int64_t Kr = r1 - r0;
+  const int64_t M = a.M, N = a.N;
+  const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+
+  const char* X = reinterpret_cast<const char*>(a.A);
+  const char* D = reinterpret_cast<const char*>(a.B);
+  BufRes ra, rb;
+  ra.init(X + (r0 * a.lda + m0) * 2, Kr * a.lda * 2 - m0 * 2);
+  rb.init(D + (r0 * a.ldb + n0) * 2, Kr * a.ldb * 2 - n0 * 2);
+  Loader<BM, BK, false, NW> la;
+  Loader<BN, BK, false, NW> lb;
+  la.init_mn(a.lda, false, M - m0);
+  lb.init_mn(a.ldb, false, N - n0);
+  auto issue = [&](char* stage, int kt) {
+    const int k0 = kt * BK;
+    la.issue(stage, [&](int) -> const BufRes& { return ra; }, k0, Kr, a.lda);
+    lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb; }, k0, Kr, a.ldb);
+  };
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm0 = (wave / WN) * (BM / WM);
+  int bcol[FN];
+  block_cols<BN, WN, FN, false>(wave % WN, bcol);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = (int)((Kr + BK - 1) / BK);
+  k_loop<NS, STAGE>(smem, nk, Loader<BM, BK, false, NW>::PER + Loader<BN, BK, false, NW>::PER, issue,
+                    [&](const char* st) { mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc); });
+
+  wgrad_epilogue<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int BK, int NS, int KIND, int EPI>
+hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
+  const int tiles_n_cols = EPI == gemm::EPI_SWIGLU_FWD ? BN / 2 : BN;
+  a.tiles_n = (int)((a.N + tiles_n_cols - 1) / tiles_n_cols);
+  a.tiles_m = (int)((rows_max + BM - 1) / BM) + a.groups;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const size_t lds = (size_t)NS * (BM + BN) * BK * 2;
+  auto kern = gemm3_rows_kernel<BM, BN, WM, WN, BK, NS, KIND, EPI>;
+  static hipError_t prep = prepare_lds(kern, lds);
+  if (prep != hipSuccess) return prep;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+hipError_t launch_wgrad(Args a, hipStream_t st) {
+  a.tiles_m = (int)((a.M + BM - 1) / BM);
+  a.tiles_n = (int)((a.N + BN - 1) / BN);
+  const int64_t grid = (int64_t)a.groups * a.tiles_m * a.tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const size_t lds = (size_t)NS * (BM + BN) * BK * 2;
+  auto kern = gemm3_wgrad_kernel<BM, BN, WM, WN, BK, NS, EPI>;
+  static hipError_t prep = prepare_lds(kern, lds);
+  if (prep != hipSuccess) return prep;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
+  return hipGetLastError();
+}
+
+#ifndef MOE_GEMM3_CFG
+#define MOE_GEMM3_CFG 256, 256, 2, 4, 64, 2
+#endif
+
+// Whether the direct-load kernels take this launch: the K split of the SwiGLU
+// dgrad (gate | up weights) must fall on a stage boundary.
+bool supports(const Args& a) {
+  constexpr int cfg[] = {MOE_GEMM3_CFG};
+  const int BK = cfg[4];
+  return a.b_split == 0 || a.b_split % BK == 0;
+}
+
+hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hipStream_t st) {
+  using namespace gemm;
+  if (kind == KIND_FWD) {
+    switch (epi) {
+      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
+      case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t run_wgrad_bf16(int epi, const Args& a, hipStream_t st) {
+  using namespace gemm;
+  if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG, EPI_STORE>(a, st);
+  if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG, EPI_STORE_SPLITN>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gemm3
+}  // namespace moe

@@ -1,0 +1,184 @@
+// Device helpers shared by the grouped-GEMM kernels (internal to libmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "gemm.h"
+
+namespace moe {
+namespace gemm_common {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int GM = 8;                      // row-tiles per ordering group
+constexpr uint32_t kOOB = 0x7FFFFFF0u;     // an offset beyond every extent
+constexpr int64_t kMaxExtent = 0x7FFF0000; // extents stay below kOOB
+constexpr int kRsrcWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 family
+
+// A buffer resource over [base, base + bytes): loads at offsets at or past
+// the extent return zeros (hardware range check).
+struct BufRes {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ void init(const void* base, int64_t bytes) {
+    const int64_t n = bytes <= 0 ? 0 : (bytes > kMaxExtent ? kMaxExtent : bytes);
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+  }
+  __device__ __forceinline__ u32x4 ld(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+};
+
+// Workgroup id -> linear tile id such that each XCD's workgroups (dispatched
+// round-robin over the 8 XCDs) get consecutive tile ids (bijection).
+__device__ __forceinline__ int xcd_remap(int hw, int num) {
+  const int q = num >> 3, r = num & 7;
+  const int xcd = hw & 7, local = hw >> 3;
+  const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  return base + local;
+}
+
+// Linear tile id -> (row tile, column tile), walking GM row tiles per column
+// so that concurrently running tiles share panels in L2.
+__device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt) {
+  const int span = GM * tiles_n;
+  const int gid = lin / span;
+  const int first = gid * GM;
+  const int gsz = min(tiles_m - first, GM);
+  const int rem = lin - gid * span;
+  mt = first + rem % gsz;
+  nt = rem / gsz;
+}
+
+__device__ __forceinline__ int weight_index(int g, int rr_R, int rr_L) {
+  // send slot g = q * L + l holds expert q + R * l under round-robin placement
+  return rr_R > 0 ? (g % rr_L) * rr_R + g / rr_L : g;
+}
+
+__device__ __forceinline__ float gelu_f(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * __expf(-0.5f * z * z) * 0.39894228040143268f;
+}
+__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// Row of accumulator element e (0..15) of a 32x32 MFMA block for this lane
+// (the lane holds column lane % 32).
+__device__ __forceinline__ int acc_row(int e, int lane) {
+  return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+}
+
+// Tile column of a wave's N-block j.  With SwiGLU pairing the tile's first
+// half holds gate columns and the second half the matching up columns; each
+// wave takes a gate block and the up block of the same columns, so one lane
+// holds both values of a hidden unit.
+template <int BN, int WN, int FN, bool PAIR>
+__device__ __forceinline__ void block_cols(int wn, int (&bcol)[FN]) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (PAIR)
+      bcol[j] = j < FN / 2 ? wn * (FN / 2) * 32 + j * 32 : BN / 2 + wn * (FN / 2) * 32 + (j - FN / 2) * 32;
+    else
+      bcol[j] = wn * FN * 32 + j * 32;
+  }
+}
+
+template <typename Kern>
+static hipError_t prepare_lds(Kern k, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+// Epilogue of the row-split kernels: rows [row_begin, row_end) of the group,
+// output columns n0 + tile column.
+template <typename T, int FM, int FN, bool PAIR, int EPI>
+__device__ __forceinline__ void rows_epilogue(const gemm::Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                              int wm0, int lane, int64_t row_begin, int64_t row_end, int64_t n0,
+                                              int64_t N) {
+  T* C = reinterpret_cast<T*>(a.C);
+  T* C2 = reinterpret_cast<T*>(a.C2);
+  const T* X1 = reinterpret_cast<const T*>(a.X1);
+  const int col = lane & 31;
+  if constexpr (PAIR) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const int64_t f = n0 + bcol[j] + col;
+        if (f >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t rr = row_begin + wm0 + i * 32 + acc_row(e, lane);
+          if (rr >= row_end) continue;
+          const float av = acc[i][j][e], bv = acc[i][j + FN / 2][e];
+          C[rr * a.ldc + f] = from_f32<T>(av);
+          C[rr * a.ldc + a.c_split + f] = from_f32<T>(bv);
+          C2[rr * a.ldc2 + f] = from_f32<T>(av * sigmoid_f(av) * bv);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + bcol[j] + col;
+        if (n >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t rr = row_begin + wm0 + i * 32 + acc_row(e, lane);
+          if (rr >= row_end) continue;
+          const float v = acc[i][j][e];
+          if constexpr (EPI == gemm::EPI_STORE) {
+            C[rr * a.ldc + n] = from_f32<T>(v);
+          } else if constexpr (EPI == gemm::EPI_GELU_FWD) {
+            C[rr * a.ldc + n] = from_f32<T>(v);
+            C2[rr * a.ldc2 + n] = from_f32<T>(gelu_f(v));
+          } else if constexpr (EPI == gemm::EPI_GELU_BWD) {
+            const float z = to_f32(X1[rr * a.ldx + n]);
+            C[rr * a.ldc + n] = from_f32<T>(v * gelu_grad_f(z));
+          } else if constexpr (EPI == gemm::EPI_SWIGLU_BWD) {
+            const float av = to_f32(X1[rr * a.ldx + n]);
+            const float bv = to_f32(X1[rr * a.ldx + a.c_split + n]);
+            const float s = sigmoid_f(av);
+            C[rr * a.ldc + n] = from_f32<T>(v * bv * s * (1.0f + av * (1.0f - s)));
+            C[rr * a.ldc + a.c_split + n] = from_f32<T>(v * av * s);
+          }
+        }
+      }
+  }
+}
+
+// Epilogue of the wgrad kernels: weight set wi, rows m0 + ..., columns
+// n0 + ...; EPI_STORE_SPLITN sends columns >= c_split to C2.
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void wgrad_epilogue(const gemm::Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                               int wm0, int lane, int wi, int64_t m0, int64_t n0, int64_t M,
+                                               int64_t N) {
+  T* C = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride;
+  T* C2 = a.C2 ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride : nullptr;
+  const int col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + bcol[j] + col;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm0 + i * 32 + acc_row(e, lane);
+        if (m >= M) continue;
+        const T v = from_f32<T>(acc[i][j][e]);
+        if (EPI == gemm::EPI_STORE_SPLITN && n >= a.c_split)
+          C2[m * a.ldc + (n - a.c_split)] = v;
+        else
+          C[m * a.ldc + n] = v;
+      }
+    }
+}
+
+}  // namespace gemm_common
+}  // namespace moe
