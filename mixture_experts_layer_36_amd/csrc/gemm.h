@@ -32,6 +32,7 @@ struct Args {
   int groups = 0;
   int rr_R = 0, rr_L = 1;   // round-robin slot -> expert map (rr_R = 0: identity)
   int tiles_m = 0, tiles_n = 0;
+  int gm = 8;               // row tiles per ordering group (L2 reuse of column panels)
 };
 
 template <typename T>

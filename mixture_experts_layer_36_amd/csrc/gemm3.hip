@@ -146,24 +146,22 @@ struct Loader {
       voff[i] = (uint32_t)(((int64_t)k * ld + col) * 2);
     }
   }
-  // Issue the loads of a stage.  KC: K range [k0, K); MN: K rows [k0, Kvalid).
+  // Issue load i (0 <= i < PER) of a stage.  KC: K range [k0, Klim);
+  // MN: K rows [k0, Klim).
   template <typename ResOf>
-  __device__ __forceinline__ void issue(char* stage, const ResOf& res_of_panel, int k0, int64_t Klim,
-                                        int64_t ld) {
+  __device__ __forceinline__ void issue_one(int i, char* stage, const ResOf& res_of_panel, int k0, int64_t Klim,
+                                            int64_t ld) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = i * NW + wave;
-      char* dst = stage + u * 1024;
-      if constexpr (KC) {
-        const bool ok = k0 + kcol[i] < Klim;
-        lds_load16(res_of_panel(0), dst, ok ? voff[i] : kOOB, (uint32_t)(k0 * 2));
-      } else {
-        constexpr int KB = BK / 4;
-        const int panel = u / KB;
-        const bool ok = colok[i] && (k0 + krow[i] < Klim);
-        lds_load16(res_of_panel(panel), dst, ok ? voff[i] : kOOB, (uint32_t)((int64_t)k0 * ld * 2));
-      }
+    const int u = i * NW + wave;
+    char* dst = stage + u * 1024;
+    if constexpr (KC) {
+      const bool ok = k0 + kcol[i] < Klim;
+      lds_load16(res_of_panel(0), dst, ok ? voff[i] : kOOB, (uint32_t)(k0 * 2));
+    } else {
+      constexpr int KB = BK / 4;
+      const int panel = u / KB;
+      const bool ok = colok[i] && (k0 + krow[i] < Klim);
+      lds_load16(res_of_panel(panel), dst, ok ? voff[i] : kOOB, (uint32_t)((int64_t)k0 * ld * 2));
     }
   }
 };
@@ -227,9 +225,9 @@ __device__ __forceinline__ u32x4 frag(uint32_t tile, int row, int s, int lane) {
 
 // MFMA over one stage (BK / 16 k-steps), fragments of step s+1 read while step
 // s multiplies.
-template <int FM, int FN, int BK, bool AKC, bool BKC>
+template <int FM, int FN, int BK, bool AKC, bool BKC, typename Hook>
 __device__ __forceinline__ void mma_stage(const char* ta_p, const char* tb_p, int wm0, const int (&bcol)[FN],
-                                          f32x16 (&acc)[FM][FN]) {
+                                          f32x16 (&acc)[FM][FN], const Hook& after_step) {
   constexpr int STEPS = BK / 16;
   constexpr int READS = FM * (AKC ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS reads per step
   const uint32_t ta = lds_addr(ta_p), tb = lds_addr(tb_p);
@@ -260,22 +258,31 @@ __device__ __forceinline__ void mma_stage(const char* ta_p, const char* tb_p, in
                                                             __builtin_bit_cast(bf16x8, bfr[s & 1][j]),
                                                             acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    // work slotted between the steps (the next stage's global->LDS loads):
+    // spreading it keeps the MFMA pipe fed while the load path is busy
+    after_step(s);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The pipelined K loop shared by both kernels.
-template <int NS, int STAGE_BYTES, typename Issue, typename Compute>
-__device__ __forceinline__ void k_loop(char* smem, int nk, int loads_per_stage, const Issue& issue,
-                                       const Compute& compute) {
+// The pipelined K loop shared by both kernels.  issue(stage, kt, q0, q1)
+// issues loads [q0, q1) of stage kt (Q per wave); compute(stage, hook) runs
+// the MFMAs of a stage and calls hook(s) after k-step s, where a share of the
+// next stage's loads is issued.
+template <int NS, int STAGE_BYTES, int Q, int STEPS, typename Issue, typename Compute>
+__device__ __forceinline__ void k_loop(char* smem, int nk, const Issue& issue, const Compute& compute) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(smem + s * STAGE_BYTES, s);
+    if (s < nk) issue(smem + s * STAGE_BYTES, s, 0, Q);
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(NS - 2, nk - 1 - kt);
-    wait_vmcnt_dyn(ahead * loads_per_stage);
+    wait_vmcnt_dyn(ahead * Q);
     barrier();
-    if (kt + NS - 1 < nk) issue(smem + ((kt + NS - 1) % NS) * STAGE_BYTES, kt + NS - 1);
-    compute(smem + (kt % NS) * STAGE_BYTES);
+    const int next = kt + NS - 1;
+    char* next_stage = smem + (next % NS) * STAGE_BYTES;
+    compute(smem + (kt % NS) * STAGE_BYTES, [&](int s) {
+      if (next < nk) issue(next_stage, next, s * Q / STEPS, (s + 1) * Q / STEPS);
+    });
   }
 }
 
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   int mt, nt;
-  grouped_order(lin, a.tiles_m, a.tiles_n, mt, nt);
+  grouped_order(lin, a.tiles_m, a.tiles_n, mt, nt, a.gm);
   if (mt >= a.tiles_m) return;
   int g = -1;
   int64_t row_begin = 0, row_end = 0;
@@ -341,17 +348,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   else lb.init_mn(a.ldb, PAIR, N - n0);
   const bool split = BKC && a.b_split > 0;
 
-  auto issue = [&](char* stage, int kt) {
+  constexpr int QA = Loader<BM, BK, true, NW>::PER, QB = Loader<BN, BK, BKC, NW>::PER;
+  auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
-    la.issue(stage, [&](int) -> const BufRes& { return ra; }, k0, K, a.lda);
-    if constexpr (BKC) {
-      if (split && k0 >= a.b_split)
-        lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb1; }, k0 - (int)a.b_split, K - a.b_split,
-                 a.ldb);
-      else
-        lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb0; }, k0, split ? a.b_split : K, a.ldb);
-    } else {
-      lb.issue(stage + A_BYTES, [&](int p) -> const BufRes& { return (PAIR && p) ? rb1 : rb0; }, k0, K, a.ldb);
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      if (q >= q0 && q < q1) la.issue_one(q, stage, [&](int) -> const BufRes& { return ra; }, k0, K, a.lda);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (QA + q < q0 || QA + q >= q1) continue;
+      if constexpr (BKC) {
+        if (split && k0 >= a.b_split)
+          lb.issue_one(q, stage + A_BYTES, [&](int) -> const BufRes& { return rb1; }, k0 - (int)a.b_split,
+                       K - a.b_split, a.ldb);
+        else
+          lb.issue_one(q, stage + A_BYTES, [&](int) -> const BufRes& { return rb0; }, k0, split ? a.b_split : K,
+                       a.ldb);
+      } else {
+        lb.issue_one(q, stage + A_BYTES, [&](int p) -> const BufRes& { return (PAIR && p) ? rb1 : rb0; }, k0, K,
+                     a.ldb);
+      }
     }
   };
 
@@ -368,8 +384,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((K + BK - 1) / BK);
-  k_loop<NS, STAGE>(smem, nk, Loader<BM, BK, true, NW>::PER + Loader<BN, BK, BKC, NW>::PER, issue,
-                    [&](const char* st) { mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc); });
+  k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, [&](const char* st, const auto& hook) {
+    mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc, hook);
+  });
 
   rows_epilogue<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
   const int g = lin / per_g;
   if (g >= a.groups) return;
   int mt, nt;
-  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt);
+  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt, a.gm);
   const int wi = weight_index(g, a.rr_R, a.rr_L);
   const int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
   const int64_t Kr = r1 - r0;
@@ -406,10 +423,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
   Loader<BN, BK, false, NW> lb;
   la.init_mn(a.lda, false, M - m0);
   lb.init_mn(a.ldb, false, N - n0);
-  auto issue = [&](char* stage, int kt) {
+  constexpr int QA = Loader<BM, BK, false, NW>::PER, QB = Loader<BN, BK, false, NW>::PER;
+  auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
-    la.issue(stage, [&](int) -> const BufRes& { return ra; }, k0, Kr, a.lda);
-    lb.issue(stage + A_BYTES, [&](int) -> const BufRes& { return rb; }, k0, Kr, a.ldb);
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      if (q >= q0 && q < q1) la.issue_one(q, stage, [&](int) -> const BufRes& { return ra; }, k0, Kr, a.lda);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      if (QA + q >= q0 && QA + q < q1)
+        lb.issue_one(q, stage + A_BYTES, [&](int) -> const BufRes& { return rb; }, k0, Kr, a.ldb);
   };
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -425,8 +448,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((Kr + BK - 1) / BK);
-  k_loop<NS, STAGE>(smem, nk, Loader<BM, BK, false, NW>::PER + Loader<BN, BK, false, NW>::PER, issue,
-                    [&](const char* st) { mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc); });
+  k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, [&](const char* st, const auto& hook) {
+    mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc, hook);
+  });
 
   wgrad_epilogue<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
 }
@@ -466,7 +490,7 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
 }
 
 #ifndef MOE_GEMM3_CFG
-#define MOE_GEMM3_CFG 256, 256, 2, 4, 64, 2
+#define MOE_GEMM3_CFG 256, 256, 2, 4, 32, 4
 #endif
 
 // Whether the direct-load kernels take this launch: the K split of the SwiGLU

@@ -41,11 +41,11 @@ __device__ __forceinline__ int xcd_remap(int hw, int num) {
 
 // Linear tile id -> (row tile, column tile), walking GM row tiles per column
 // so that concurrently running tiles share panels in L2.
-__device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt) {
-  const int span = GM * tiles_n;
+__device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt, int gm = GM) {
+  const int span = gm * tiles_n;
   const int gid = lin / span;
-  const int first = gid * GM;
-  const int gsz = min(tiles_m - first, GM);
+  const int first = gid * gm;
+  const int gsz = min(tiles_m - first, gm);
   const int rem = lin - gid * span;
   mt = first + rem % gsz;
   nt = rem / gsz;
