@@ -271,28 +271,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_rows_kernel(Args a) {
   static_assert(!PAIR || FN % 2 == 0, "SwiGLU pairing needs an even number of N-blocks per wave");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  int mt, nt;
-  grouped_order(lin, a.tiles_m, a.tiles_n, mt, nt);
-  if (mt >= a.tiles_m) return;
-  // m-tile -> group
-  int g = -1;
+  int g = -1, nt = 0;
   int64_t row_begin = 0, row_end = 0;
-  {
-    int acc_t = 0;
-    for (int gg = 0; gg < a.groups; ++gg) {
-      const int64_t o0 = a.offsets[gg], o1 = a.offsets[gg + 1];
-      const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
-      if (mt < acc_t + nt_g) {
-        g = gg;
-        row_begin = o0 + (int64_t)(mt - acc_t) * BM;
-        row_end = o1;
-        break;
-      }
-      acc_t += nt_g;
-    }
-  }
-  if (g < 0) return;
+  if (!row_tile_of<BM>(a, g, row_begin, row_end, nt)) return;
   const int wi = weight_index(g, a.rr_R, a.rr_L);
   const int64_t K = a.K, N = a.N;
   const int64_t rows_valid = min((int64_t)BM, row_end - row_begin);

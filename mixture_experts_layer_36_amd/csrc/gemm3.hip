@@ -49,7 +49,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  // n is wave-uniform and small; dispatch to immediates
+  // n is wave-uniform; dispatch to immediates (values above the table wait
+  // for everything, which is correct, only slower)
   switch (n) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<1>(); break;
@@ -68,9 +69,38 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     case 14: wait_vmcnt<14>(); break;
     case 15: wait_vmcnt<15>(); break;
     case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
     case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    case 23: wait_vmcnt<23>(); break;
     case 24: wait_vmcnt<24>(); break;
+    case 25: wait_vmcnt<25>(); break;
+    case 26: wait_vmcnt<26>(); break;
+    case 27: wait_vmcnt<27>(); break;
+    case 28: wait_vmcnt<28>(); break;
+    case 29: wait_vmcnt<29>(); break;
+    case 30: wait_vmcnt<30>(); break;
+    case 31: wait_vmcnt<31>(); break;
     case 32: wait_vmcnt<32>(); break;
+    case 33: wait_vmcnt<33>(); break;
+    case 34: wait_vmcnt<34>(); break;
+    case 35: wait_vmcnt<35>(); break;
+    case 36: wait_vmcnt<36>(); break;
+    case 37: wait_vmcnt<37>(); break;
+    case 38: wait_vmcnt<38>(); break;
+    case 39: wait_vmcnt<39>(); break;
+    case 40: wait_vmcnt<40>(); break;
+    case 41: wait_vmcnt<41>(); break;
+    case 42: wait_vmcnt<42>(); break;
+    case 43: wait_vmcnt<43>(); break;
+    case 44: wait_vmcnt<44>(); break;
+    case 45: wait_vmcnt<45>(); break;
+    case 46: wait_vmcnt<46>(); break;
+    case 47: wait_vmcnt<47>(); break;
+    case 48: wait_vmcnt<48>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -101,7 +131,7 @@ __device__ __forceinline__ int mn_swz(int k) { return 4 * (k & 3); }
 
 // One operand's direct loads.  The stage is split into 1 KiB units; unit u of
 // the stage is issued by wave u % NW as its (u / NW)-th load.
-template <int R, int BK, bool KC, int NW>
+template <int R, int BK, bool KC, int NW, int W0 = 0>
 struct Loader {
   static constexpr int BYTES = R * BK * 2;
   static constexpr int UNITS = BYTES / 1024;
@@ -116,7 +146,7 @@ struct Loader {
   __device__ __forceinline__ void init_kc(int64_t ld) {
     constexpr int CPR = BK * 2 / 16;     // chunks per row
     constexpr int RPU = 64 / CPR;        // rows per unit
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
     const int p = lane % CPR;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -132,7 +162,7 @@ struct Loader {
   // MN: element (k, col) at k * ld + col elements from the base of the
   // resource of the column's panel (col relative to that base).
   __device__ __forceinline__ void init_mn(int64_t ld, bool pair, int64_t valid_cols) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
     constexpr int KB = BK / 4;  // units per panel (4 K rows each)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -151,7 +181,7 @@ struct Loader {
   template <typename ResOf>
   __device__ __forceinline__ void issue_one(int i, char* stage, const ResOf& res_of_panel, int k0, int64_t Klim,
                                             int64_t ld) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
     const int u = i * NW + wave;
     char* dst = stage + u * 1024;
     if constexpr (KC) {
@@ -286,12 +316,40 @@ __device__ __forceinline__ void k_loop(char* smem, int nk, const Issue& issue, c
   }
 }
 
+// Warp-specialised K loop: producer waves only issue the global->LDS loads,
+// consumer waves only read fragments and run MFMAs; both meet at one barrier
+// per stage.  A producer stalled on a busy load path then never holds back
+// the MFMA pipe of its SIMD.
+template <int NS, int STAGE_BYTES, int Q, typename Issue, typename Compute>
+__device__ __forceinline__ void k_loop_split(char* smem, int nk, bool producer, const Issue& issue,
+                                             const Compute& compute) {
+  if (producer) {
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(smem + s * STAGE_BYTES, s, 0, Q);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(NS - 2, nk - 1 - kt);
+      wait_vmcnt_dyn(ahead * Q);
+      barrier();
+      const int next = kt + NS - 1;
+      if (next < nk) issue(smem + (next % NS) * STAGE_BYTES, next, 0, Q);
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      barrier();
+      compute(smem + (kt % NS) * STAGE_BYTES, [](int) {});
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // FWD / DGRAD: rows split by group.  A = activation rows (K-contiguous).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BK, int NS, int KIND, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
-  constexpr int NW = WM * WN;
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
+__global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_rows_kernel(Args a) {
+  constexpr int NC = WM * WN;                 // consumer (MFMA) waves
+  constexpr int NW = NP > 0 ? NP : NC;        // waves issuing loads
+  constexpr int W0 = NP > 0 ? NC : 0;         // first loading wave
   constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr bool PAIR = (EPI == gemm::EPI_SWIGLU_FWD);
   constexpr bool BKC = (KIND == gemm::KIND_DGRAD);
@@ -301,27 +359,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   static_assert(BM % 128 == 0 && BN % 128 == 0 && (BK == 32 || BK == 64), "tile shape");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  int mt, nt;
-  grouped_order(lin, a.tiles_m, a.tiles_n, mt, nt, a.gm);
-  if (mt >= a.tiles_m) return;
-  int g = -1;
+  int g = -1, nt = 0;
   int64_t row_begin = 0, row_end = 0;
-  {
-    int acc_t = 0;
-    for (int gg = 0; gg < a.groups; ++gg) {
-      const int64_t o0 = a.offsets[gg], o1 = a.offsets[gg + 1];
-      const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
-      if (mt < acc_t + nt_g) {
-        g = gg;
-        row_begin = o0 + (int64_t)(mt - acc_t) * BM;
-        row_end = o1;
-        break;
-      }
-      acc_t += nt_g;
-    }
-  }
-  if (g < 0) return;
+  if (!row_tile_of<BM>(a, g, row_begin, row_end, nt)) return;
   const int wi = weight_index(g, a.rr_R, a.rr_L);
   const int64_t K = a.K, N = a.N;
   const int64_t rows_valid = min((int64_t)BM, row_end - row_begin);
@@ -341,14 +381,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
     rb1.init(B2g + n0 * a.ldb * 2, (N - n0) * a.ldb * 2);
   }
 
-  Loader<BM, BK, true, NW> la;
-  Loader<BN, BK, BKC, NW> lb;
-  la.init_kc(a.lda);
-  if constexpr (BKC) lb.init_kc(a.ldb);
-  else lb.init_mn(a.ldb, PAIR, N - n0);
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool producer = NP > 0 && wave_u >= NC;
+  const bool loads = NP == 0 || producer;
+  Loader<BM, BK, true, NW, W0> la;
+  Loader<BN, BK, BKC, NW, W0> lb;
+  if (loads) {
+    la.init_kc(a.lda);
+    if constexpr (BKC) lb.init_kc(a.ldb);
+    else lb.init_mn(a.ldb, PAIR, N - n0);
+  }
   const bool split = BKC && a.b_split > 0;
 
-  constexpr int QA = Loader<BM, BK, true, NW>::PER, QB = Loader<BN, BK, BKC, NW>::PER;
+  constexpr int QA = Loader<BM, BK, true, NW, W0>::PER, QB = Loader<BN, BK, BKC, NW, W0>::PER;
   auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
 #pragma unroll
@@ -371,7 +416,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
     }
   };
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_u % NC, lane = threadIdx.x & 63;
   const int wm0 = (wave / WN) * (BM / WM);
   int bcol[FN];
   block_cols<BN, WN, FN, PAIR>(wave % WN, bcol);
@@ -384,9 +429,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((K + BK - 1) / BK);
-  k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, [&](const char* st, const auto& hook) {
+  auto compute = [&](const char* st, const auto& hook) {
     mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc, hook);
-  });
+  };
+  if constexpr (NP > 0) {
+    k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
+    if (producer) return;
+  } else {
+    k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
+  }
 
   rows_epilogue<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
@@ -394,9 +445,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // WGRAD: C_g[M, N] = X[rows_g, M]^T . D[rows_g, N], both MN-contiguous.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
-  constexpr int NW = WM * WN;
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
+__global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_wgrad_kernel(Args a) {
+  constexpr int NC = WM * WN;
+  constexpr int NW = NP > 0 ? NP : NC;
+  constexpr int W0 = NP > 0 ? NC : 0;
   constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -419,11 +472,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
   BufRes ra, rb;
   ra.init(X + (r0 * a.lda + m0) * 2, Kr * a.lda * 2 - m0 * 2);
   rb.init(D + (r0 * a.ldb + n0) * 2, Kr * a.ldb * 2 - n0 * 2);
-  Loader<BM, BK, false, NW> la;
-  Loader<BN, BK, false, NW> lb;
-  la.init_mn(a.lda, false, M - m0);
-  lb.init_mn(a.ldb, false, N - n0);
-  constexpr int QA = Loader<BM, BK, false, NW>::PER, QB = Loader<BN, BK, false, NW>::PER;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool producer = NP > 0 && wave_u >= NC;
+  Loader<BM, BK, false, NW, W0> la;
+  Loader<BN, BK, false, NW, W0> lb;
+  if (NP == 0 || producer) {
+    la.init_mn(a.lda, false, M - m0);
+    lb.init_mn(a.ldb, false, N - n0);
+  }
+  constexpr int QA = Loader<BM, BK, false, NW, W0>::PER, QB = Loader<BN, BK, false, NW, W0>::PER;
   auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
 #pragma unroll
@@ -435,7 +492,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
         lb.issue_one(q, stage + A_BYTES, [&](int) -> const BufRes& { return rb; }, k0, Kr, a.ldb);
   };
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_u % NC, lane = threadIdx.x & 63;
   const int wm0 = (wave / WN) * (BM / WM);
   int bcol[FN];
   block_cols<BN, WN, FN, false>(wave % WN, bcol);
@@ -448,9 +505,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((Kr + BK - 1) / BK);
-  k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, [&](const char* st, const auto& hook) {
+  auto compute = [&](const char* st, const auto& hook) {
     mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc, hook);
-  });
+  };
+  if constexpr (NP > 0) {
+    k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
+    if (producer) return;
+  } else {
+    k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
+  }
 
   wgrad_epilogue<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
 }
@@ -458,7 +521,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BK, int NS, int KIND, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
 hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   const int tiles_n_cols = EPI == gemm::EPI_SWIGLU_FWD ? BN / 2 : BN;
   a.tiles_n = (int)((a.N + tiles_n_cols - 1) / tiles_n_cols);
@@ -467,14 +530,14 @@ hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)NS * (BM + BN) * BK * 2;
-  auto kern = gemm3_rows_kernel<BM, BN, WM, WN, BK, NS, KIND, EPI>;
+  auto kern = gemm3_rows_kernel<BM, BN, WM, WN, BK, NS, NP, KIND, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + NP)), lds, st, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 hipError_t launch_wgrad(Args a, hipStream_t st) {
   a.tiles_m = (int)((a.M + BM - 1) / BM);
   a.tiles_n = (int)((a.N + BN - 1) / BN);
@@ -482,38 +545,43 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)NS * (BM + BN) * BK * 2;
-  auto kern = gemm3_wgrad_kernel<BM, BN, WM, WN, BK, NS, EPI>;
+  auto kern = gemm3_wgrad_kernel<BM, BN, WM, WN, BK, NS, NP, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + NP)), lds, st, a);
   return hipGetLastError();
 }
 
-#ifndef MOE_GEMM3_CFG
-#define MOE_GEMM3_CFG 256, 256, 2, 4, 32, 4
-#endif
+// Tile configurations (BM, BN, WM, WN, BK, NS, NP), chosen per launch kind
+// from measurements of the Mixtral-sized expert GEMMs (d 4096, F 14336):
+//  * CFG_WIDE: 256x256 tile, 8 compute waves, K-step 32, 4-stage ring; every
+//    wave also issues its share of the loads.
+//  * CFG_PAIR / CFG_DGRAD: 4 compute waves plus 4 waves that only issue the
+//    direct-to-LDS loads, K-step 64, 3-stage ring.  Faster for the paired
+//    gate|up forward GEMM and the plain dgrad GEMM.
+#define MOE_GEMM3_CFG_WIDE 256, 256, 2, 4, 32, 4, 0
+#define MOE_GEMM3_CFG_PAIR 128, 256, 1, 4, 64, 3, 4
+#define MOE_GEMM3_CFG_DGRAD 256, 128, 2, 2, 64, 3, 4
 
 // Whether the direct-load kernels take this launch: the K split of the SwiGLU
 // dgrad (gate | up weights) must fall on a stage boundary.
-bool supports(const Args& a) {
-  constexpr int cfg[] = {MOE_GEMM3_CFG};
-  const int BK = cfg[4];
-  return a.b_split == 0 || a.b_split % BK == 0;
-}
+bool supports(const Args& a) { return a.b_split == 0 || a.b_split % 32 == 0; }
 
 hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hipStream_t st) {
   using namespace gemm;
   if (kind == KIND_FWD) {
     switch (epi) {
-      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
-      case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
+      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_FWD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
+      case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG_PAIR, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
     }
   } else {
     switch (epi) {
-      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
-      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+      case EPI_STORE:
+        if (a.b_split % 64 == 0) return launch_rows<MOE_GEMM3_CFG_DGRAD, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
+        return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   }
   return hipErrorInvalidValue;
@@ -521,8 +589,8 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
 
 hipError_t run_wgrad_bf16(int epi, const Args& a, hipStream_t st) {
   using namespace gemm;
-  if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG, EPI_STORE>(a, st);
-  if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG, EPI_STORE_SPLITN>(a, st);
+  if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG_WIDE, EPI_STORE>(a, st);
+  if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG_WIDE, EPI_STORE_SPLITN>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -51,6 +51,35 @@ __device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n,
   nt = rem / gsz;
 }
 
+// Row-split launches size the grid for the largest possible row count, since
+// the per-group row counts live on the device.  Each workgroup first counts the
+// row tiles the groups really hold; surplus workgroups exit, and the XCD remap
+// and the grouped order run over the real tiles only, so the work spreads over
+// every XCD whatever the row count.  Returns false for a surplus workgroup.
+template <int BM>
+__device__ __forceinline__ bool row_tile_of(const gemm::Args& a, int& g, int64_t& row_begin, int64_t& row_end,
+                                            int& nt) {
+  int real_m = 0;
+  for (int gg = 0; gg < a.groups; ++gg) real_m += (int)((a.offsets[gg + 1] - a.offsets[gg] + BM - 1) / BM);
+  const int real = real_m * a.tiles_n;
+  if ((int)blockIdx.x >= real) return false;
+  int mt;
+  grouped_order(xcd_remap(blockIdx.x, real), real_m, a.tiles_n, mt, nt, a.gm);
+  int acc_t = 0;
+  for (int gg = 0; gg < a.groups; ++gg) {
+    const int64_t o0 = a.offsets[gg], o1 = a.offsets[gg + 1];
+    const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
+    if (mt < acc_t + nt_g) {
+      g = gg;
+      row_begin = o0 + (int64_t)(mt - acc_t) * BM;
+      row_end = o1;
+      return true;
+    }
+    acc_t += nt_g;
+  }
+  return false;
+}
+
 __device__ __forceinline__ int weight_index(int g, int rr_R, int rr_L) {
   // send slot g = q * L + l holds expert q + R * l under round-robin placement
   return rr_R > 0 ? (g % rr_L) * rr_R + g / rr_L : g;
