@@ -2,109 +2,228 @@
 // every device scores its local tokens with the replicated router g(x);
 // 用于分布式 MoE 的主流框架与库: a top-k gate with k chosen experts).
 //
-// One token is handled by a group of S lanes of a wave (S = 8 or 16).  Lane s
-// streams 16-byte pieces of the token's row (coalesced: the S lanes cover
-// S*16 contiguous bytes) and accumulates partial logits for all EP (padded)
-// experts against a K-chunk of the router weight staged in LDS as fp32.
-// A butterfly reduce-scatter over the S lanes then leaves lane s with the
-// complete logits of experts [s*EP/S, (s+1)*EP/S); softmax statistics and the
-// k rounds of arg-max are wave shuffles over the group.  Comparisons order by
-// (logit descending, expert index ascending), so equal logits go to the lower
-// index.  fp32 accumulation throughout; the summation order is fixed, so the
-// logits are deterministic.
+// A workgroup owns 64 tokens, one per lane, and its W waves (16, or 8 for more
+// than 16 experts) split the model width: wave w takes the 128-byte column
+// chunks w, w+W, w+2W, ... of the tokens' rows.  Per chunk the wave loads the
+// 64 rows coalesced (8 lanes per 128-byte row piece), transposes them through its own slice of LDS (XOR
+// swizzled, so both the writes and the per-lane row reads are free of bank
+// conflicts) and then each lane holds 64 consecutive bf16 (or 32 fp32) values
+// of its own token.  The router weight rows of the chunk are the same for
+// every lane, so they come in through wave-uniform scalar loads and feed the
+// dot products straight from scalar registers: bf16 uses the two-term
+// fp32-accumulating dot instruction on (x[k], x[k+1]) . (W[k][e], W[k+1][e]),
+// fp32 plain FMAs.  The W per-wave partial logits are then summed in a fixed
+// binary tree through LDS, so the logits are deterministic.  Lane t of wave 0
+// finally holds all logits of its token and does the softmax statistics and
+// the k rounds of arg-max sequentially, ordering by (logit descending, expert
+// index ascending): equal logits go to the lower index.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <typename T, int S, int EP>
-__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, const T* __restrict__ w,
-                                                   const float* __restrict__ bias, float* __restrict__ logits,
-                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                                                   int64_t Tn, int d, int E, int k, int gating) {
-  constexpr int V = Vec16<T>::N;
-  constexpr int KC = S * V;       // K rows per LDS chunk
-  constexpr int TPB = 256 / S;    // tokens per block
-  constexpr int EPL = EP / S;     // experts per lane after the reduce-scatter
-  constexpr int WP = EP + 4;      // LDS row pitch in floats (breaks bank aliasing)
-  __shared__ __attribute__((aligned(16))) float wl[KC * WP];
+namespace {
 
-  const int tid = threadIdx.x;
-  const int s = tid % S;
-  const int64_t t = (int64_t)blockIdx.x * TPB + tid / S;
-  const bool tok_ok = t < Tn;
+constexpr int kRouteTokens = 64;
+
+// Waves per workgroup: more waves hide more load latency; wide rows (E > 16)
+// need more registers per wave, so fewer of them fit.
+template <int EP> constexpr int route_waves() { return EP <= 16 ? 16 : 8; }
+template <int EP> constexpr size_t route_lds() {
+  constexpr size_t stage = (size_t)route_waves<EP>() * kRouteTokens * 128;
+  constexpr size_t red = (size_t)(route_waves<EP>() / 2) * EP * kRouteTokens * 4;
+  return stage > red ? stage : red;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// 16-bit packs (lo(a), lo(b)) and (hi(a), hi(b)) of wave-uniform operands.
+// The first is selected as the scalar pack instruction from a vector build;
+// the second has no such pattern, so it is written out.
+__device__ __forceinline__ uint32_t s_pack_ll(uint32_t a, uint32_t b) {
+  const u16x2_t v = {(unsigned short)a, (unsigned short)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t s_pack_hh(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
+  return r;
+}
+
+// Router weight pair (W[k][e], W[k+1][e]) as one dword of two bf16: rows are
+// E elements long, so the pair is gathered from two rows with scalar loads.
+// With E even and k even both rows start on a dword, and the pair is one
+// scalar pack of the dwords holding experts (e & ~1, e | 1) of rows k, k+1.
+template <int EP, bool FULL>
+__device__ __forceinline__ uint32_t w_pair(const uint32_t* __restrict__ wd, int k, int e, int E) {
+  if constexpr (FULL) {
+    const uint32_t d0 = wd[(k * EP + e) >> 1], d1 = wd[((k + 1) * EP + e) >> 1];
+    return (e & 1) ? s_pack_hh(d0, d1) : s_pack_ll(d0, d1);
+  } else {
+    const int ee = e < E ? e : E - 1;
+    const int i0 = k * E + ee, i1 = i0 + E;
+    const uint32_t d0 = wd[i0 >> 1], d1 = wd[i1 >> 1];
+    const uint32_t lo = (i0 & 1) ? (d0 >> 16) : (d0 & 0xffffu);
+    const uint32_t hi = (i1 & 1) ? (d1 >> 16) : (d1 & 0xffffu);
+    return e < E ? (lo | (hi << 16)) : 0u;
+  }
+}
+
+template <int EP, bool FULL>
+__device__ __forceinline__ float w_f32(const float* __restrict__ w, int k, int e, int E) {
+  const int En = FULL ? EP : E;
+  const int ee = FULL ? e : (e < E ? e : E - 1);
+  const float v = w[k * En + ee];
+  return (FULL || e < E) ? v : 0.0f;
+}
+
+}  // namespace
+
+template <typename T, int EP, bool FULL>
+__global__ __launch_bounds__(route_waves<EP>() * 64) void route_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                                const float* __restrict__ bias,
+                                                                float* __restrict__ logits,
+                                                                int32_t* __restrict__ topk_idx,
+                                                                float* __restrict__ topk_w, int64_t Tn, int d, int E,
+                                                                int k, int gating) {
+  constexpr int KC = 128 / sizeof(T);  // elements of a 128-byte row piece
+  constexpr int kRouteWaves = route_waves<EP>();
+  constexpr int STAGE = kRouteTokens * 128;
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // route_lds<EP>() bytes
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
+  char* stage = lds + wave * STAGE;
+  const int nchunks = (d + KC - 1) / KC;
+
+  // load r of a chunk: lanes 8r'..8r'+7 cover the 128-byte piece of token
+  // 8r + r', lane l taking its 16-byte part l % 8.
+  const int sub = lane & 7, trow = lane >> 3;
+  auto load_chunk = [&](int c, u32x4 (&v)[8]) {
+    const int col = c * KC + sub * (16 / (int)sizeof(T));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t t = t0 + r * 8 + trow;
+      v[r] = (t < Tn && col < d) ? ld16(x + t * d + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   float acc[EP];
 #pragma unroll
   for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
 
-  for (int k0 = 0; k0 < d; k0 += KC) {
-    const int kx = k0 + s * V;
-    float xv[V];
-    if (tok_ok && kx < d) {
-      unpack16<T>(ld16(x + t * d + kx), xv);
-    } else {
+  u32x4 nx[8];
+  int c = wave;
+  if (c < nchunks) load_chunk(c, nx);
+  for (; c < nchunks; c += kRouteWaves) {
+    u32x4 cur[8];
 #pragma unroll
-      for (int i = 0; i < V; ++i) xv[i] = 0.0f;
+    for (int r = 0; r < 8; ++r) cur[r] = nx[r];
+    if (c + kRouteWaves < nchunks) load_chunk(c + kRouteWaves, nx);
+    // transpose through LDS: row = token, 16-byte slot swizzled by row % 8
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = r * 8 + trow;
+      st16(stage + row * 128 + ((sub ^ (row & 7)) << 4), cur[r]);
     }
-    __syncthreads();
-    for (int i = tid; i < KC * EP; i += 256) {
-      const int r = i / EP, e = i % EP;
-      float v = 0.0f;
-      if (k0 + r < d && e < E) v = to_f32(w[(int64_t)(k0 + r) * E + e]);
-      wl[r * WP + e] = v;
-    }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // piece j of the lane's own row: 16 bytes = 4 dwords of x, each a pair
+    // (bf16) or a single value (fp32); the pieces are read one at a time so
+    // that every register index is static.
+    const int kb = c * KC;
+    const int npiece = min(KC, d - kb) / (16 / (int)sizeof(T));  // d is a multiple of 8
+#pragma unroll 2
+    for (int j = 0; j < npiece; ++j) {
+      const u32x4 xj = ld16(stage + lane * 128 + ((j ^ (lane & 7)) << 4));
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t* wd = reinterpret_cast<const uint32_t*>(w);
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const float* wr = wl + (s * V + i) * WP;
+        for (int q = 0; q < 4; ++q) {
+          const int kk = kb + 8 * j + 2 * q;
+          // through a scalar: this compiler's bit_cast of a vector element
+          // expression reads element 0 whatever the index
+          const uint32_t xu = xj[q];
+          const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xu);
 #pragma unroll
-      for (int e = 0; e < EP; e += 4) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + e);
-        acc[e] += xv[i] * wv[0];
-        acc[e + 1] += xv[i] * wv[1];
-        acc[e + 2] += xv[i] * wv[2];
-        acc[e + 3] += xv[i] * wv[3];
+          for (int e = 0; e < EP; ++e) {
+            const bf16x2_t wp = __builtin_bit_cast(bf16x2_t, w_pair<EP, FULL>(wd, kk, e, E));
+            acc[e] = __builtin_amdgcn_fdot2_f32_bf16(xp, wp, acc[e], false);
+          }
+          // wide rows: keep one pair's weight rows live in scalar registers
+          if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        const float* wf = reinterpret_cast<const float*>(w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kk = kb + 4 * j + q;
+          const float xv = __uint_as_float(xj[q]);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[e] = fmaf(xv, w_f32<EP, FULL>(wf, kk, e, E), acc[e]);
+          if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
+    // the next chunk's LDS writes stay behind this chunk's reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // Reduce-scatter over the S lanes: after the step with mask m the lane
-  // keeps the half of its experts selected by bit m of s.
+  // fixed-order tree sum of the per-wave partial logits
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();
 #pragma unroll
-  for (int m = S / 2; m >= 1; m >>= 1) {
-    const int half = EP * m / S;
-    const bool upper = (s & m) != 0;
+  for (int h = kRouteWaves / 2; h >= 1; h >>= 1) {
+    if (wave >= h && wave < 2 * h) {
 #pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? acc[i] : acc[i + half];
-      const float keep = upper ? acc[i + half] : acc[i];
-      acc[i] = keep + __shfl_xor(send, m, kWave);
+      for (int e = 0; e < EP; ++e) red[((wave - h) * EP + e) * kRouteTokens + lane] = acc[e];
     }
-  }
-  const int e0 = s * EPL;
-  float lv[EPL];
-  bool valid[EPL];
+    __syncthreads();
+    if (wave < h) {
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = e0 + i;
-    valid[i] = e < E;
-    lv[i] = valid[i] ? acc[i] + (bias ? bias[e] : 0.0f) : -INFINITY;
-    if (tok_ok && valid[i]) logits[t * E + e] = lv[i];
+      for (int e = 0; e < EP; ++e) acc[e] += red[(wave * EP + e) * kRouteTokens + lane];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  const int64_t t = t0 + lane;
+  if (t >= Tn) return;
+
+  float lv[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) {
+    const bool ok = FULL || e < E;
+    lv[e] = ok ? acc[e] + (bias ? bias[e] : 0.0f) : -INFINITY;
+  }
+  float* lrow = logits + t * E;
+  if constexpr (FULL) {
+#pragma unroll
+    for (int e = 0; e < EP; e += 4) st16(lrow + e, u32x4{__float_as_uint(lv[e]), __float_as_uint(lv[e + 1]),
+                                                          __float_as_uint(lv[e + 2]), __float_as_uint(lv[e + 3])});
+  } else {
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (e < E) lrow[e] = lv[e];
   }
 
   // softmax statistics over all experts of the token
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, lv[i]);
-  mx = group_max<S>(mx);
+  for (int e = 0; e < EP; ++e) mx = fmaxf(mx, lv[e]);
   float z = 0.0f;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) z += valid[i] ? __expf(lv[i] - mx) : 0.0f;
-  z = group_sum<S>(z);
+  for (int e = 0; e < EP; ++e)
+    if (FULL || e < E) z += __expf(lv[e] - mx);
 
-  // k rounds of arg-max by (value desc, index asc)
-  unsigned taken = 0u;
+  // k rounds of arg-max by (value desc, index asc): a strictly greater value
+  // replaces the running best while scanning upwards in the index
+  uint64_t taken = 0;
   float sel_v[8];
   int sel_e[8];
 #pragma unroll
@@ -113,63 +232,60 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
     sel_e[j] = 0;
     if (j < k) {
       float bv = -INFINITY;
-      int be = 0x7fffffff;
+      int be = -1;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        if (valid[i] && !((taken >> i) & 1u) && (lv[i] > bv || be == 0x7fffffff)) {
-          bv = lv[i];
-          be = e0 + i;
+      for (int e = 0; e < EP; ++e) {
+        const bool ok = (FULL || e < E) && !((taken >> e) & 1u);
+        if (ok && (be < 0 || lv[e] > bv)) {
+          bv = lv[e];
+          be = e;
         }
       }
-#pragma unroll
-      for (int m = 1; m < S; m <<= 1) {
-        const float ov = __shfl_xor(bv, m, kWave);
-        const int oe = __shfl_xor(be, m, kWave);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (be >= e0 && be < e0 + EPL) taken |= 1u << (be - e0);
+      if (be >= 0) taken |= (uint64_t)1 << be;
       sel_v[j] = bv;
       sel_e[j] = be;
     }
   }
 
-  if (tok_ok && s == 0) {
-    float den = 0.0f;
-    if (gating != 0) {
+  float den = 0.0f;
+  if (gating != 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) den += __expf(sel_v[j] - sel_v[0]);
-    }
+    for (int j = 0; j < 8; ++j)
+      if (j < k) den += __expf(sel_v[j] - sel_v[0]);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        const float g = gating == 0 ? __expf(sel_v[j] - mx) / z : __expf(sel_v[j] - sel_v[0]) / den;
-        topk_idx[t * k + j] = sel_e[j];
-        topk_w[t * k + j] = g;
-      }
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      const float g = gating == 0 ? __expf(sel_v[j] - mx) / z : __expf(sel_v[j] - sel_v[0]) / den;
+      topk_idx[t * k + j] = sel_e[j];
+      topk_w[t * k + j] = g;
     }
   }
 }
 
-template <typename T, int S, int EP>
+template <typename T, int EP>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  constexpr int TPB = 256 / S;
-  const int64_t blocks = (a.T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((route_kernel<T, S, EP>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const T*)a.x, (const T*)a.w, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k,
-                     a.gating);
+  const int64_t blocks = (a.T + kRouteTokens - 1) / kRouteTokens;
+  if (blocks <= 0) return hipSuccess;
+  constexpr size_t lds = route_lds<EP>();
+  auto kern = a.E == EP ? route_kernel<T, EP, true> : route_kernel<T, EP, false>;
+  static const hipError_t prep_full = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(route_kernel<T, EP, true>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static const hipError_t prep_part = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(route_kernel<T, EP, false>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (prep_full != hipSuccess) return prep_full;
+  if (prep_part != hipSuccess) return prep_part;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(route_waves<EP>() * 64), lds, st, (const T*)a.x,
+                     (const T*)a.w, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k, a.gating);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_route_dt(const RouteArgs& a, hipStream_t st) {
-  if (a.E <= 8) return launch_route_t<T, 8, 8>(a, st);
-  if (a.E <= 16) return launch_route_t<T, 16, 16>(a, st);
-  if (a.E <= 32) return launch_route_t<T, 16, 32>(a, st);
-  return launch_route_t<T, 16, 64>(a, st);
+  if (a.E <= 8) return launch_route_t<T, 8>(a, st);
+  if (a.E <= 16) return launch_route_t<T, 16>(a, st);
+  if (a.E <= 32) return launch_route_t<T, 32>(a, st);
+  return launch_route_t<T, 64>(a, st);
 }
 
 hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st) {
