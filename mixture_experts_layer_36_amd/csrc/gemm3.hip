@@ -342,11 +342,85 @@ __device__ __forceinline__ void k_loop_split(char* smem, int nk, bool producer, 
   }
 }
 
+// Fragments of one whole stage, read ahead of the MFMAs that use them.
+template <int FM, int FN, int BK>
+struct StageFrags {
+  u32x4 a[BK / 16][FM];
+  u32x4 b[BK / 16][FN];
+};
+
+template <int FM, int FN, int BK, bool AKC, bool BKC>
+__device__ __forceinline__ void read_stage(const char* ta_p, const char* tb_p, int wm0, const int (&bcol)[FN],
+                                           StageFrags<FM, FN, BK>& f) {
+  const uint32_t ta = lds_addr(ta_p), tb = lds_addr(tb_p);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) f.a[s][i] = frag<AKC, BK>(ta, wm0 + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.b[s][j] = frag<BKC, BK>(tb, bcol[j], s, lane);
+  }
+}
+
+template <int FM, int FN, int BK>
+__device__ __forceinline__ void mma_frags(const StageFrags<FM, FN, BK>& f, f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[s][i]),
+                                                            __builtin_bit_cast(bf16x8, f.b[s][j]), acc[i][j], 0,
+                                                            0, 0);
+}
+
+// Ping-pong K loop.  The workgroup's waves form two groups with one wave of
+// each on every SIMD (waves w and w + NC/2).  Per stage a wave runs a memory
+// phase (issue its share of the loads of the stage NS-1 ahead, read all of
+// this stage's fragments into registers) and then a compute phase (only
+// MFMAs); group 1 runs one phase behind group 0, so in every phase one wave
+// per SIMD issues MFMAs while the other feeds the load path.  Phases are
+// separated by workgroup barriers (2 per stage, the same count for both
+// groups).  Loads of stage s are issued in the memory phases of stage
+// s - (NS-1); each wave waits for its own loads of stage t+1 at the end of
+// its memory phase of stage t, so stage t+1 is complete and visible when
+// group 0 starts reading it, and the slot reloaded in a phase was last read
+// two phases earlier.
+template <int NS, int STAGE_BYTES, int Q, typename Issue, typename Read, typename Mma>
+__device__ __forceinline__ void k_loop_pingpong(char* smem, int nk, int group, const Issue& issue, const Read& read,
+                                                const Mma& mma) {
+  constexpr int D = NS - 1;
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nk) issue(smem + s * STAGE_BYTES, s, 0, Q);
+  wait_vmcnt_dyn((min(D, nk) - 1) * Q);
+  if (group == 1) barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int next = kt + D;
+    if (next < nk) issue(smem + (next % NS) * STAGE_BYTES, next, 0, Q);
+    read(smem + (kt % NS) * STAGE_BYTES);
+    wait_vmcnt_dyn(max(0, min(D - 1, nk - 2 - kt)) * Q);
+    wait_lgkmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mma();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) barrier();
+}
+
+constexpr int kPingPong = -1;  // NP value selecting the ping-pong loop
+
 // ---------------------------------------------------------------------------
 // FWD / DGRAD: rows split by group.  A = activation rows (K-contiguous).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
-__global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_rows_kernel(Args a) {
+__global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows_kernel(Args a) {
   constexpr int NC = WM * WN;                 // consumer (MFMA) waves
   constexpr int NW = NP > 0 ? NP : NC;        // waves issuing loads
   constexpr int W0 = NP > 0 ? NC : 0;         // first loading wave
@@ -383,7 +457,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_rows_kernel(Args a)
 
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool producer = NP > 0 && wave_u >= NC;
-  const bool loads = NP == 0 || producer;
+  const bool loads = NP <= 0 || producer;
   Loader<BM, BK, true, NW, W0> la;
   Loader<BN, BK, BKC, NW, W0> lb;
   if (loads) {
@@ -432,7 +506,13 @@ __global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_rows_kernel(Args a)
   auto compute = [&](const char* st, const auto& hook) {
     mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc, hook);
   };
-  if constexpr (NP > 0) {
+  if constexpr (NP == kPingPong) {
+    StageFrags<FM, FN, BK> fr;
+    k_loop_pingpong<NS, STAGE, QA + QB>(
+        smem, nk, wave_u / (NC / 2), issue,
+        [&](const char* st) { read_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, fr); },
+        [&]() { mma_frags<FM, FN, BK>(fr, acc); });
+  } else if constexpr (NP > 0) {
     k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
     if (producer) return;
   } else {
@@ -446,7 +526,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_rows_kernel(Args a)
 // WGRAD: C_g[M, N] = X[rows_g, M]^T . D[rows_g, N], both MN-contiguous.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
-__global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_wgrad_kernel(Args a) {
+__global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgrad_kernel(Args a) {
   constexpr int NC = WM * WN;
   constexpr int NW = NP > 0 ? NP : NC;
   constexpr int W0 = NP > 0 ? NC : 0;
@@ -476,7 +556,7 @@ __global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_wgrad_kernel(Args a
   const bool producer = NP > 0 && wave_u >= NC;
   Loader<BM, BK, false, NW, W0> la;
   Loader<BN, BK, false, NW, W0> lb;
-  if (NP == 0 || producer) {
+  if (NP <= 0 || producer) {
     la.init_mn(a.lda, false, M - m0);
     lb.init_mn(a.ldb, false, N - n0);
   }
@@ -508,7 +588,13 @@ __global__ __launch_bounds__(64 * (WM * WN + NP)) void gemm3_wgrad_kernel(Args a
   auto compute = [&](const char* st, const auto& hook) {
     mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc, hook);
   };
-  if constexpr (NP > 0) {
+  if constexpr (NP == kPingPong) {
+    StageFrags<FM, FN, BK> fr;
+    k_loop_pingpong<NS, STAGE, QA + QB>(
+        smem, nk, wave_u / (NC / 2), issue,
+        [&](const char* st) { read_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, fr); },
+        [&]() { mma_frags<FM, FN, BK>(fr, acc); });
+  } else if constexpr (NP > 0) {
     k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
     if (producer) return;
   } else {
@@ -533,7 +619,7 @@ hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   auto kern = gemm3_rows_kernel<BM, BN, WM, WN, BK, NS, NP, KIND, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + NP)), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + (NP > 0 ? NP : 0))), lds, st, a);
   return hipGetLastError();
 }
 
@@ -548,20 +634,18 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
   auto kern = gemm3_wgrad_kernel<BM, BN, WM, WN, BK, NS, NP, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + NP)), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + (NP > 0 ? NP : 0))), lds, st, a);
   return hipGetLastError();
 }
 
 // Tile configurations (BM, BN, WM, WN, BK, NS, NP), chosen per launch kind
 // from measurements of the Mixtral-sized expert GEMMs (d 4096, F 14336):
-//  * CFG_WIDE: 256x256 tile, 8 compute waves, K-step 32, 4-stage ring; every
-//    wave also issues its share of the loads.
-//  * CFG_PAIR / CFG_DGRAD: 4 compute waves plus 4 waves that only issue the
-//    direct-to-LDS loads, K-step 64, 3-stage ring.  Faster for the paired
-//    gate|up forward GEMM and the plain dgrad GEMM.
+//  * CFG_PP: 256x256 tile, 8 waves in two ping-pong groups, K-step 32,
+//    4-stage ring: every row-split kind (forward, dgrad).
+//  * CFG_WIDE: the same tile with all 8 waves in lockstep: wgrad, whose
+//    operands both need transposing reads.
+#define MOE_GEMM3_CFG_PP 256, 256, 2, 4, 32, 4, -1
 #define MOE_GEMM3_CFG_WIDE 256, 256, 2, 4, 32, 4, 0
-#define MOE_GEMM3_CFG_PAIR 128, 256, 1, 4, 64, 3, 4
-#define MOE_GEMM3_CFG_DGRAD 256, 128, 2, 2, 64, 3, 4
 
 // Whether the direct-load kernels take this launch: the K split of the SwiGLU
 // dgrad (gate | up weights) must fall on a stage boundary.
@@ -571,17 +655,15 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
   using namespace gemm;
   if (kind == KIND_FWD) {
     switch (epi) {
-      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_FWD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
-      case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG_PAIR, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
+      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
+      case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
     }
   } else {
     switch (epi) {
-      case EPI_STORE:
-        if (a.b_split % 64 == 0) return launch_rows<MOE_GEMM3_CFG_DGRAD, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
-        return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
-      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
-      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_WIDE, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+      case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
+      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   }
   return hipErrorInvalidValue;
