@@ -10,15 +10,21 @@ Prints ONE JSON line (stdout):
   value       tokens per second of the whole step (T / step time)
   roofline    the grouped expert GEMM (all its launches in a step): algorithmic
               FLOPs (3 x 2 n d F m, plus shared experts) / its event-measured
-              time, against the bf16 dense MFMA peak
+              time, against the bf16 dense MFMA peak; `traffic` is the HBM
+              bytes per step of those launches from hardware counters
+              (profiles/gemm_traffic_<workload>.txt), reported only while the
+              GEMM sources still hash to the ones the counters were taken on
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
   kernels     per-entry-point times and achieved rates (events around each call)
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_bf16]
+       [--calibrate-copy MIB]   (also runs a plain device copy of MIB MiB, for
+                                 scaling memory counters in a profiler run)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +41,38 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+GEMM_SOURCES = ("gemm3.hip", "gemm_common.h", "gemm.h", "common.h", "moe_api.hip")
+
+
+def gemm_source_hash():
+    """sha256 over the sources that define the grouped GEMM kernels and their launches."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(HERE, "mixture_experts_layer_36_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gemm_traffic(workload):
+    """HBM bytes per step of the grouped GEMM launches, from the counter
+    summary of this workload, or None when it is missing or was taken on
+    other GEMM sources."""
+    path = os.path.join(HERE, "profiles", f"gemm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    return {"read_bytes": int(kv["read_bytes_per_step"]), "write_bytes": int(kv["write_bytes_per_step"]),
+            "bytes": int(kv["read_bytes_per_step"]) + int(kv["write_bytes_per_step"]),
+            "source": os.path.relpath(path, HERE)}
 
 
 def algorithmic(wl, n, T_kept):
@@ -93,6 +131,7 @@ def main():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
@@ -190,7 +229,22 @@ def main():
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
                 "per_step_flops": gemm_flops, "per_step_ms": round(gemm_ms, 4)}
+    traffic = gemm_traffic(wl.name)
+    if traffic is not None:
+        roofline["traffic"] = traffic["bytes"]
+        roofline["traffic_detail"] = traffic
     permute_gbs = kernels["dispatch"]["GBps"]
+
+    if args.calibrate_copy > 0:
+        # a plain elementwise copy (read N bytes, write N bytes) of known size
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x neg over {nbytes} bytes (read {nbytes}, write {nbytes} each)")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
