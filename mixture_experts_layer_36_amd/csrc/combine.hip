@@ -11,186 +11,320 @@
 
 namespace moe {
 
+// One wave per token row.  The row indices and gate weights of the token are
+// wave-uniform (scalar loads); each lane takes the 16-byte chunks lane,
+// lane + 64, ... of the row, U at a time, and issues all loads of a round
+// (U chunks of each of the <= KMAX gathered rows) before it combines them.
+constexpr int kRowWaves = 4;  // waves (tokens) per workgroup
+
+template <int KMAX> constexpr int row_unroll() { return KMAX <= 2 ? 4 : 2; }
+
 // y[t] = sum_j g[t,j] * y_perm[row_of[t,j]] (+ y_shared[t])
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm, const int32_t* __restrict__ row_of,
-                                                      const float* __restrict__ topk_w,
-                                                      const T* __restrict__ y_shared, T* __restrict__ y, int64_t Tn,
-                                                      int d, int k, int tpb) {
-  constexpr int V = Vec16<T>::N;
+template <typename T, int KMAX>
+__global__ __launch_bounds__(64 * kRowWaves) void combine_kernel(const T* __restrict__ y_perm,
+                                                                 const int32_t* __restrict__ row_of,
+                                                                 const float* __restrict__ topk_w,
+                                                                 const T* __restrict__ y_shared, T* __restrict__ y,
+                                                                 int64_t Tn, int d, int k) {
+  constexpr int V = Vec16<T>::N, U = row_unroll<KMAX>();
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= Tn) return;
   const int nch = d / V;
-  const int total = tpb * nch;
-  const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  for (int i = threadIdx.x; i < total; i += 256) {
-    const int tl = i / nch, c = i - tl * nch;
-    const int64_t t = t0 + tl;
-    if (t >= Tn) break;
-    float acc[V];
+  int rows[KMAX];
+  float g[KMAX];
 #pragma unroll
-    for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = row_of[t * k + j];
-      if (r < 0) continue;
-      const float g = topk_w[t * k + j];
-      float v[V];
-      unpack16<T>(ld16(y_perm + (int64_t)r * d + (int64_t)c * V), v);
+  for (int j = 0; j < KMAX; ++j) {
+    rows[j] = j < k ? row_of[t * k + j] : -1;
+    g[j] = rows[j] >= 0 ? topk_w[t * k + j] : 0.0f;
+  }
+  for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+    u32x4 v[KMAX][U], sh[U];
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] += g * v[q];
+    for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        v[j][u] = (rows[j] >= 0 && c < nch) ? ld16(y_perm + (int64_t)rows[j] * d + (int64_t)c * V)
+                                            : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      sh[u] = (y_shared && c < nch) ? ld16(y_shared + t * d + (int64_t)c * V) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (y_shared) {
-      float v[V];
-      unpack16<T>(ld16(y_shared + t * d + (int64_t)c * V), v);
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] += v[q];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nch) break;
+      float acc[V], f[V];
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rows[j] < 0) continue;
+        unpack16<T>(v[j][u], f);
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] += g[j] * f[q];
+      }
+      if (y_shared) {
+        unpack16<T>(sh[u], f);
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[q] += f[q];
+      }
+      st16(y + t * d + (int64_t)c * V, pack16<T>(acc));
     }
-    st16(y + t * d + (int64_t)c * V, pack16<T>(acc));
   }
 }
 
-// One wave per token: dy_perm[row] = g * dy[t]; d_topk_w[t,j] = <dy[t], y_perm[row]>.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
-                                                          const int32_t* __restrict__ row_of,
-                                                          const float* __restrict__ topk_w, T* __restrict__ dy_perm,
-                                                          float* __restrict__ d_topk_w, int64_t Tn, int d, int k) {
-  constexpr int V = Vec16<T>::N;
+// dy_perm[row] = g * dy[t]; d_topk_w[t,j] = <dy[t], y_perm[row]>, one wave per token.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(64 * kRowWaves) void combine_bwd_kernel(const T* __restrict__ dy,
+                                                                     const T* __restrict__ y_perm,
+                                                                     const int32_t* __restrict__ row_of,
+                                                                     const float* __restrict__ topk_w,
+                                                                     T* __restrict__ dy_perm,
+                                                                     float* __restrict__ d_topk_w, int64_t Tn, int d,
+                                                                     int k) {
+  constexpr int V = Vec16<T>::N, U = row_unroll<KMAX>();
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nch = d / V;
-  int rows[8];
-  float g[8], dot[8];
+  int rows[KMAX];
+  float g[KMAX], dot[KMAX];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     rows[j] = j < k ? row_of[t * k + j] : -1;
     g[j] = rows[j] >= 0 ? topk_w[t * k + j] : 0.0f;
     dot[j] = 0.0f;
   }
-  for (int c = lane; c < nch; c += 64) {
-    float dv[V];
-    unpack16<T>(ld16(dy + t * d + (int64_t)c * V), dv);
+  for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+    u32x4 dv[U], ov[KMAX][U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (rows[j] < 0) continue;
-      float ov[V], sv[V];
-      unpack16<T>(ld16(y_perm + (int64_t)rows[j] * d + (int64_t)c * V), ov);
-      float p = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      dv[u] = c < nch ? ld16(dy + t * d + (int64_t)c * V) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int q = 0; q < V; ++q) {
-        p += dv[q] * ov[q];
-        sv[q] = g[j] * dv[q];
+    for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        ov[j][u] = (rows[j] >= 0 && c < nch) ? ld16(y_perm + (int64_t)rows[j] * d + (int64_t)c * V)
+                                             : u32x4{0u, 0u, 0u, 0u};
       }
-      dot[j] += p;
-      st16(dy_perm + (int64_t)rows[j] * d + (int64_t)c * V, pack16<T>(sv));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nch) break;
+      float df[V], of[V], sv[V];
+      unpack16<T>(dv[u], df);
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rows[j] < 0) continue;
+        unpack16<T>(ov[j][u], of);
+        float p = 0.0f;
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          p += df[q] * of[q];
+          sv[q] = g[j] * df[q];
+        }
+        dot[j] += p;
+        st16(dy_perm + (int64_t)rows[j] * d + (int64_t)c * V, pack16<T>(sv));
+      }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < KMAX; ++j) {
     if (j >= k) break;
     const float s = group_sum<64>(dot[j]);
     if (lane == 0) d_topk_w[t * k + j] = rows[j] >= 0 ? s : 0.0f;
   }
 }
 
+// CPT consecutive elements (CPT * sizeof(T) bytes, CPT a power of two <= 8).
+template <typename T, int CPT>
+__device__ __forceinline__ void load_cols(const T* p, float (&v)[CPT]) {
+  if constexpr (CPT * sizeof(T) == 16) {
+    unpack16<T>(ld16(p), v);
+  } else if constexpr (CPT * sizeof(T) == 8) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    if constexpr (sizeof(T) == 2) {
+      v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xffff0000u);
+      v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xffff0000u);
+    } else {
+      v[0] = __uint_as_float(w[0]); v[1] = __uint_as_float(w[1]);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) v[c] = to_f32(p[c]);
+  }
+}
+// load_cols of p when pred, else zeros.  The load is unconditional (from the
+// valid address `fallback` when !pred) and the zeros are a select, so no
+// branch forces the wait for the load right after it.
+template <typename T, int CPT>
+__device__ __forceinline__ void load_cols_if(bool pred, const T* p, const T* fallback, float (&v)[CPT]) {
+  load_cols<T, CPT>(pred ? p : fallback, v);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) v[c] = pred ? v[c] : 0.0f;
+}
+template <typename T, int CPT>
+__device__ __forceinline__ void store_cols(T* p, const float (&v)[CPT]) {
+  if constexpr (CPT * sizeof(T) == 16) {
+    st16(p, pack16<T>(v));
+  } else if constexpr (CPT * sizeof(T) == 8 && sizeof(T) == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                                         bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) p[c] = from_f32<T>(v[c]);
+  }
+}
+
 // dx[t, i] = sum_j dx_perm[row_of[t,j], i] + sum_e dl[t,e] * W_r[i,e] (+ dx_add[t, i]).
-// A thread owns CPT consecutive columns and keeps their router-weight rows in
-// registers while it walks the block's tokens; the tokens' dlogits are staged
-// in LDS.
-template <typename T, int EP, int CPT>
+// A lane owns CPT consecutive columns and keeps their router-weight rows in
+// registers (fp32; CPT * EP = 64 values, one 128-byte stretch of W_r when
+// E == EP, read with 16-byte loads) while its wave walks tpw tokens, two at a
+// time.  The tokens' row indices and dlogits are the same for the whole wave
+// and come in through scalar loads; the gathered rows of both tokens are
+// loaded before they are summed.
+template <typename T, int EP, int CPT, bool FULL, int KMAX>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dx_perm,
                                                            const int32_t* __restrict__ row_of,
                                                            const float* __restrict__ dl, const T* __restrict__ w_r,
                                                            const T* __restrict__ dx_add, T* __restrict__ dx,
                                                            int64_t Tn, int d, int E, int k, int tpw) {
-  extern __shared__ __attribute__((aligned(16))) float dls[];  // [tpw][EP]
+  static_assert(CPT * EP == 64, "64 router weights per lane");
+  constexpr int TU = 2;  // tokens per round
   const int64_t t0 = (int64_t)blockIdx.x * tpw;
   const int i0 = (blockIdx.y * 256 + threadIdx.x) * CPT;
-  for (int q = threadIdx.x; q < tpw * EP; q += 256) {
-    const int tl = q / EP, e = q % EP;
-    const int64_t t = t0 + tl;
-    dls[q] = (t < Tn && e < E) ? dl[t * E + e] : 0.0f;
-  }
-  __syncthreads();
-  if (i0 >= d) return;
+  const bool col_ok = i0 < d;  // d is a multiple of 8: a lane's CPT columns are all in or all out
   float wr[CPT][EP];
+  if constexpr (FULL) {
+    // rows i0 .. i0+CPT-1 of W_r are CPT*EP contiguous elements
+    constexpr int NV = CPT * EP / Vec16<T>::N;
+    const T* wp = col_ok ? w_r + (int64_t)i0 * EP : w_r;  // unconditional loads, zeros by select
+    u32x4 raw[NV];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+    for (int v = 0; v < NV; ++v) raw[v] = ld16(wp + v * Vec16<T>::N);
 #pragma unroll
-    for (int e = 0; e < EP; ++e) wr[c][e] = e < E ? to_f32(w_r[(int64_t)(i0 + c) * E + e]) : 0.0f;
+    for (int v = 0; v < NV; ++v) {
+      float f[Vec16<T>::N];
+      unpack16<T>(raw[v], f);
+#pragma unroll
+      for (int q = 0; q < Vec16<T>::N; ++q) {
+        const int idx = v * Vec16<T>::N + q;
+        wr[idx / EP][idx % EP] = col_ok ? f[q] : 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) wr[c][e] = (col_ok && e < E) ? to_f32(w_r[(int64_t)(i0 + c) * E + e]) : 0.0f;
+  }
 
-  for (int tl = 0; tl < tpw; ++tl) {
-    const int64_t t = t0 + tl;
-    if (t >= Tn) break;
-    float acc[CPT];
+  // U tokens at a time: every load of the round issued before any sum; the
+  // tail round repeats the last token (in range, result not stored)
+  const int64_t tlast = (t0 + tpw < Tn ? t0 + tpw : Tn) - 1;
+  for (int64_t tb = t0; tb <= tlast; tb += TU) {
+    int64_t tt[TU];
+    int rows[TU][KMAX];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = row_of[t * k + j];
-      if (r < 0) continue;
-      const T* p = dx_perm + (int64_t)r * d + i0;
+    for (int u = 0; u < TU; ++u) {
+      tt[u] = tb + u <= tlast ? tb + u : tlast;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] += to_f32(p[c]);
+      for (int j = 0; j < KMAX; ++j) rows[u][j] = j < k ? row_of[tt[u] * k + j] : -1;
     }
-    const float* dlt = dls + tl * EP;
+    float g[TU][KMAX][CPT], add[TU][CPT];
 #pragma unroll
-    for (int e = 0; e < EP; e += 4) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(dlt + e);
+    for (int u = 0; u < TU; ++u) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
-        acc[c] += lv[0] * wr[c][e] + lv[1] * wr[c][e + 1] + lv[2] * wr[c][e + 2] + lv[3] * wr[c][e + 3];
+      for (int j = 0; j < KMAX; ++j) {
+        const bool ok = col_ok && rows[u][j] >= 0;
+        load_cols_if<T, CPT>(ok, dx_perm + (int64_t)(ok ? rows[u][j] : 0) * d + i0, dx_perm, g[u][j]);
+      }
+      const bool aok = dx_add != nullptr && col_ok;
+      load_cols_if<T, CPT>(aok, (aok ? dx_add : dx_perm) + (aok ? tt[u] * d + i0 : 0), dx_perm, add[u]);
     }
-    if (dx_add) {
-      const T* p = dx_add + t * d + i0;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] += to_f32(p[c]);
+    for (int u = 0; u < TU; ++u) {
+      float acc[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] += g[u][j][c];
+      const float* dlt = dl + tt[u] * (FULL ? EP : E);
+#pragma unroll
+      for (int e = 0; e < EP; ++e) {
+        const float lv = (FULL || e < E) ? dlt[e] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = fmaf(lv, wr[c][e], acc[c]);
+      }
+      // one token's dlogits at a time in scalar registers (up to 64)
+      if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] += add[u][c];
+      if (col_ok && tb + u <= tlast) store_cols<T, CPT>(dx + tt[u] * d + i0, acc);
     }
-    T* o = dx + t * d + i0;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) o[c] = from_f32<T>(acc[c]);
   }
 }
 
-hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st) {
-  const int tpb = tokens_per_copy_block(a.d, bf16_dtype ? 2 : 4);
-  const int64_t blocks = (a.T + tpb - 1) / tpb;
-  if (bf16_dtype)
-    hipLaunchKernelGGL((combine_kernel<bf16>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)a.y_perm,
-                       a.row_of, a.topk_w, (const bf16*)a.y_shared, (bf16*)a.y, a.T, (int)a.d, a.k, tpb);
+template <typename T, int KMAX>
+static hipError_t launch_combine_t(const CombineArgs& a, bool backward, hipStream_t st) {
+  const int64_t blocks = (a.T + kRowWaves - 1) / kRowWaves;
+  if (blocks <= 0) return hipSuccess;
+  if (!backward)
+    hipLaunchKernelGGL((combine_kernel<T, KMAX>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
+                       (const T*)a.y_perm, a.row_of, a.topk_w, (const T*)a.y_shared, (T*)a.y, a.T, (int)a.d, a.k);
   else
-    hipLaunchKernelGGL((combine_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st, (const float*)a.y_perm,
-                       a.row_of, a.topk_w, (const float*)a.y_shared, (float*)a.y, a.T, (int)a.d, a.k, tpb);
+    hipLaunchKernelGGL((combine_bwd_kernel<T, KMAX>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
+                       (const T*)a.dy, (const T*)a.y_perm, a.row_of, a.topk_w, (T*)a.dy_perm, a.d_topk_w, a.T,
+                       (int)a.d, a.k);
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_combine_dt(const CombineArgs& a, bool backward, hipStream_t st) {
+  return a.k <= 2 ? launch_combine_t<T, 2>(a, backward, st) : launch_combine_t<T, 8>(a, backward, st);
+}
+
+hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st) {
+  return bf16_dtype ? launch_combine_dt<bf16>(a, false, st) : launch_combine_dt<float>(a, false, st);
+}
+
 hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t st) {
-  const int64_t blocks = (a.T + 3) / 4;
-  if (bf16_dtype)
-    hipLaunchKernelGGL((combine_bwd_kernel<bf16>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)a.dy,
-                       (const bf16*)a.y_perm, a.row_of, a.topk_w, (bf16*)a.dy_perm, a.d_topk_w, a.T, (int)a.d, a.k);
-  else
-    hipLaunchKernelGGL((combine_bwd_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st, (const float*)a.dy,
-                       (const float*)a.y_perm, a.row_of, a.topk_w, (float*)a.dy_perm, a.d_topk_w, a.T, (int)a.d,
-                       a.k);
+  return bf16_dtype ? launch_combine_dt<bf16>(a, true, st) : launch_combine_dt<float>(a, true, st);
+}
+
+template <typename T, int EP, int CPT, int KMAX>
+static hipError_t launch_dbwd_k(const DispatchBwdArgs& a, hipStream_t st) {
+  constexpr int TPW = 16;  // tokens per workgroup
+  const int64_t bx = (a.T + TPW - 1) / TPW;
+  const int by = (int)((a.d + 256 * CPT - 1) / (256 * CPT));
+  if (bx <= 0) return hipSuccess;
+  auto kern = a.E == EP ? dispatch_bwd_kernel<T, EP, CPT, true, KMAX> : dispatch_bwd_kernel<T, EP, CPT, false, KMAX>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)bx, by), dim3(256), 0, st, (const T*)a.dx_perm, a.row_of, a.dlogits,
+                     (const T*)a.w_router, (const T*)a.dx_add, (T*)a.dx, a.T, (int)a.d, a.E, a.k, TPW);
   return hipGetLastError();
 }
 
 template <typename T, int EP, int CPT>
 static hipError_t launch_dbwd_t(const DispatchBwdArgs& a, hipStream_t st) {
-  constexpr int TPW = 32;
-  const int64_t bx = (a.T + TPW - 1) / TPW;
-  const int by = (int)((a.d + 256 * CPT - 1) / (256 * CPT));
-  hipLaunchKernelGGL((dispatch_bwd_kernel<T, EP, CPT>), dim3((unsigned)bx, by), dim3(256),
-                     TPW * EP * sizeof(float), st, (const T*)a.dx_perm, a.row_of, a.dlogits, (const T*)a.w_router,
-                     (const T*)a.dx_add, (T*)a.dx, a.T, (int)a.d, a.E, a.k, TPW);
-  return hipGetLastError();
+  return a.k <= 2 ? launch_dbwd_k<T, EP, CPT, 2>(a, st) : launch_dbwd_k<T, EP, CPT, 8>(a, st);
 }
 
+// CPT * EP router weights per lane: 64 registers
 template <typename T>
 static hipError_t launch_dbwd_dt(const DispatchBwdArgs& a, hipStream_t st) {
   if (a.E <= 8) return launch_dbwd_t<T, 8, 8>(a, st);
-  if (a.E <= 16) return launch_dbwd_t<T, 16, 8>(a, st);
-  if (a.E <= 32) return launch_dbwd_t<T, 32, 4>(a, st);
-  return launch_dbwd_t<T, 64, 2>(a, st);
+  if (a.E <= 16) return launch_dbwd_t<T, 16, 4>(a, st);
+  if (a.E <= 32) return launch_dbwd_t<T, 32, 2>(a, st);
+  return launch_dbwd_t<T, 64, 1>(a, st);
 }
 
 hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st) {

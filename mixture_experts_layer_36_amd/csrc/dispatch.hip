@@ -130,39 +130,58 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void permute_copy_kernel(const T* __restrict__ x, const int32_t* __restrict__ row_of,
-                                                           T* __restrict__ x_perm, int64_t Tn, int d, int k,
-                                                           int tpb) {
-  constexpr int V = Vec16<T>::N;
+// One wave per token: its kept rows (wave-uniform scalar loads) receive the
+// token's row; each lane moves the 16-byte chunks lane, lane + 64, ... of it,
+// U at a time, with the U loads issued before the stores.
+constexpr int kCopyWaves = 4;
+
+template <typename T, int KMAX>
+__global__ __launch_bounds__(64 * kCopyWaves) void permute_copy_kernel(const T* __restrict__ x,
+                                                                       const int32_t* __restrict__ row_of,
+                                                                       T* __restrict__ x_perm, int64_t Tn, int d,
+                                                                       int k) {
+  constexpr int V = Vec16<T>::N, U = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kCopyWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= Tn) return;
+  int rows[KMAX];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    rows[j] = j < k ? row_of[t * k + j] : -1;
+    any |= rows[j] >= 0;
+  }
+  if (!any) return;  // a fully dropped token is not read
   const int nch = d / V;
-  const int total = tpb * nch;
-  const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  for (int i = threadIdx.x; i < total; i += 256) {
-    const int tl = i / nch, c = i - tl * nch;
-    const int64_t t = t0 + tl;
-    if (t >= Tn) break;
-    int rows[8];
-    bool any = false;
+  for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+    u32x4 v[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      rows[j] = j < k ? row_of[t * k + j] : -1;
-      any |= rows[j] >= 0;
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      v[u] = c < nch ? ld16(x + t * d + (int64_t)c * V) : u32x4{0u, 0u, 0u, 0u};
     }
-    if (!any) continue;
-    const u32x4 v = ld16(x + t * d + (int64_t)c * V);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (rows[j] >= 0) st16(x_perm + (int64_t)rows[j] * d + (int64_t)c * V, v);
+    for (int j = 0; j < KMAX; ++j) {
+      if (rows[j] < 0) continue;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nch) st16(x_perm + (int64_t)rows[j] * d + (int64_t)c * V, v[u]);
+      }
+    }
   }
 }
 
-int tokens_per_copy_block(int64_t d, int elem_bytes) {
-  const int64_t nch = d * elem_bytes / 16;
-  int64_t tpb = (256 * 8) / (nch > 0 ? nch : 1);
-  if (tpb < 1) tpb = 1;
-  if (tpb > 64) tpb = 64;
-  return (int)tpb;
+template <typename T>
+static void launch_permute_copy(const DispatchArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.T + kCopyWaves - 1) / kCopyWaves;
+  if (blocks <= 0) return;
+  if (a.k <= 2)
+    hipLaunchKernelGGL((permute_copy_kernel<T, 2>), dim3((unsigned)blocks), dim3(64 * kCopyWaves), 0, st,
+                       (const T*)a.x, a.row_of, (T*)a.x_perm, a.T, (int)a.d, a.k);
+  else
+    hipLaunchKernelGGL((permute_copy_kernel<T, 8>), dim3((unsigned)blocks), dim3(64 * kCopyWaves), 0, st,
+                       (const T*)a.x, a.row_of, (T*)a.x_perm, a.T, (int)a.d, a.k);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st) {
@@ -180,15 +199,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t s
                      a.block_base, a.expert_start, a.row_of, a.assign_of_row);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int eb = bf16_dtype ? 2 : 4;
-  const int tpb = tokens_per_copy_block(a.d, eb);
-  const int64_t blocks = (a.T + tpb - 1) / tpb;
-  if (bf16_dtype)
-    hipLaunchKernelGGL((permute_copy_kernel<bf16>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)a.x,
-                       a.row_of, (bf16*)a.x_perm, a.T, (int)a.d, a.k, tpb);
-  else
-    hipLaunchKernelGGL((permute_copy_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st, (const float*)a.x,
-                       a.row_of, (float*)a.x_perm, a.T, (int)a.d, a.k, tpb);
+  if (bf16_dtype) launch_permute_copy<bf16>(a, st);
+  else launch_permute_copy<float>(a, st);
   return hipGetLastError();
 }
 

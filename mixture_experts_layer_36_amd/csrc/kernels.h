@@ -49,7 +49,6 @@ hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t
 hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st);
 
-int tokens_per_copy_block(int64_t d, int elem_bytes);
 int router_wgrad_blocks(int64_t T);
 
 }  // namespace moe

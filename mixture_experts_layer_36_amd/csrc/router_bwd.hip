@@ -9,7 +9,7 @@
 //                          dl[e_j] = g_j * (dg_j - sum_m g_m dg_m), 0 elsewhere
 // router wgrad: dW_r = x^T dl as a deterministic two-stage reduction over
 //   tokens: each block of tokens writes an fp32 partial [d, E], then the
-//   partials are summed in block order.
+//   partials are summed in block order (at most 64 blocks).
 #include "common.h"
 #include "kernels.h"
 
@@ -48,50 +48,97 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict
   if (valid) dl[t * E + lane] = out;
 }
 
-// partial[b][i][e] = sum over tokens t of block b of x[t, i] * dl[t, e]
-template <typename T, int EP>
-__global__ __launch_bounds__(256) void router_wgrad_partial_kernel(const T* __restrict__ x,
-                                                                   const float* __restrict__ dl,
-                                                                   float* __restrict__ partial, int64_t Tn, int d,
-                                                                   int E, int tb) {
-  constexpr int TS = 64;  // tokens staged per step
-  __shared__ __attribute__((aligned(16))) float dls[TS * EP];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int b = blockIdx.y;
-  const int64_t tbeg = (int64_t)b * tb;
-  const int64_t tend = tbeg + tb < Tn ? tbeg + tb : Tn;
-  float acc[EP];
+// CPT consecutive elements of a row as floats (16, 8, 4 or 2 bytes).
+template <typename T, int CPT>
+__device__ __forceinline__ void load_row_cols(const T* p, float (&v)[CPT]) {
+  if constexpr (CPT * sizeof(T) == 16) {
+    unpack16<T>(ld16(p), v);
+  } else {
 #pragma unroll
-  for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
-  for (int64_t t0 = tbeg; t0 < tend; t0 += TS) {
-    __syncthreads();
-    for (int q = threadIdx.x; q < TS * EP; q += 256) {
-      const int tl = q / EP, e = q % EP;
-      const int64_t t = t0 + tl;
-      dls[q] = (t < tend && e < E) ? dl[t * E + e] : 0.0f;
-    }
-    __syncthreads();
-    const int nt = (int)(tend - t0 < TS ? tend - t0 : TS);
-    if (i < d) {
-      for (int tl = 0; tl < nt; ++tl) {
-        const float xv = to_f32(x[(t0 + tl) * d + i]);
-        const float* dlt = dls + tl * EP;
-#pragma unroll
-        for (int e = 0; e < EP; e += 4) {
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(dlt + e);
-          acc[e] += xv * lv[0];
-          acc[e + 1] += xv * lv[1];
-          acc[e + 2] += xv * lv[2];
-          acc[e + 3] += xv * lv[3];
-        }
-      }
-    }
+    for (int c = 0; c < CPT; ++c) v[c] = to_f32(p[c]);
   }
-  if (i < d) {
-    float* p = partial + ((int64_t)b * d + i) * E;
+}
+
+// partial[b][i][e] = sum over tokens t of token block b of x[t, i] * dl[t, e].
+// A lane owns CPT = 64 / EP consecutive columns (all EP experts: 64 fp32
+// accumulators); the 4 waves of a workgroup take consecutive quarters of the
+// block's tokens, 4 tokens per round with their x loads issued first, the
+// tokens' dlogits coming in through wave-uniform scalar loads.  The waves'
+// sums are added in wave order through LDS, so the partials are deterministic.
+constexpr int kRwgWaves = 4;
+
+template <typename T, int EP, int CPT, bool FULL>
+__global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_partial_kernel(const T* __restrict__ x,
+                                                                              const float* __restrict__ dl,
+                                                                              float* __restrict__ partial,
+                                                                              int64_t Tn, int d, int E, int tw) {
+  static_assert(CPT * EP == 64, "64 accumulators per lane");
+  constexpr int TU = 4;
+  __shared__ float red[kRwgWaves - 1][64][64];  // [wave - 1][accumulator][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i0 = (blockIdx.x * 64 + lane) * CPT;
+  const bool col_ok = i0 < d;  // d is a multiple of 8: a lane's columns are all in or all out
+  const int64_t tbeg = ((int64_t)blockIdx.y * kRwgWaves + wave) * tw;
+  const int64_t tend = tbeg + tw < Tn ? tbeg + tw : Tn;
+  const int Es = FULL ? EP : E;
+  float acc[CPT][EP];
 #pragma unroll
-    for (int e = 0; e < EP; ++e)
-      if (e < E) p[e] = acc[e];
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[c][e] = 0.0f;
+  // one token: x[t, i0..] (unconditional load, zeros by select for lanes
+  // past the last column) times the token's dlogits
+  auto token = [&](int64_t t, const float (&xr)[CPT]) {
+    const float* dlt = dl + t * Es;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      const float lv = (FULL || e < E) ? dlt[e] : 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c][e] = fmaf(xr[c], lv, acc[c][e]);
+    }
+    // one token's dlogits at a time in scalar registers (up to 64)
+    if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_x = [&](int64_t t, float (&xr)[CPT]) {
+    load_row_cols<T, CPT>(col_ok ? x + t * d + i0 : x, xr);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) xr[c] = col_ok ? xr[c] : 0.0f;
+  };
+  int64_t t = tbeg;
+  // full rounds of TU tokens: all TU loads issued before the FMAs
+  for (; t + TU <= tend; t += TU) {
+    float xv[TU][CPT];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) load_x(t + u, xv[u]);
+#pragma unroll
+    for (int u = 0; u < TU; ++u) token(t + u, xv[u]);
+  }
+  for (; t < tend; ++t) {
+    float xr[CPT];
+    load_x(t, xr);
+    token(t, xr);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) red[wave - 1][c * EP + e][lane] = acc[c][e];
+  }
+  __syncthreads();
+  if (wave == 0 && col_ok) {
+#pragma unroll
+    for (int w = 0; w < kRwgWaves - 1; ++w)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[c][e] += red[w][c * EP + e][lane];
+    float* p = partial + ((int64_t)blockIdx.y * d + i0) * E;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        if (FULL || e < E) p[c * E + e] = acc[c][e];
   }
 }
 
@@ -107,10 +154,16 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 
 template <typename T, int EP>
 static hipError_t launch_rwg(const RouteBwdArgs& a, hipStream_t st) {
+  constexpr int CPT = 64 / EP;
   const int nb = router_wgrad_blocks(a.T);
-  const int tb = (int)((a.T + nb - 1) / nb);
-  hipLaunchKernelGGL((router_wgrad_partial_kernel<T, EP>), dim3((unsigned)((a.d + 255) / 256), nb), dim3(256), 0, st,
-                     (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d, a.E, tb);
+  const int tw = (int)((a.T + (int64_t)nb * kRwgWaves - 1) / ((int64_t)nb * kRwgWaves));  // tokens per wave
+  const dim3 grid((unsigned)((a.d + 64 * CPT - 1) / (64 * CPT)), nb);
+  if (a.E == EP)
+    hipLaunchKernelGGL((router_wgrad_partial_kernel<T, EP, CPT, true>), grid, dim3(64 * kRwgWaves), 0, st,
+                       (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d, a.E, tw);
+  else
+    hipLaunchKernelGGL((router_wgrad_partial_kernel<T, EP, CPT, false>), grid, dim3(64 * kRwgWaves), 0, st,
+                       (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d, a.E, tw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t dE = a.d * a.E;
