@@ -27,6 +27,9 @@
 //
 // Workgroup: WM x WN waves, tile BM x BN, MFMA v_mfma_f32_32x32x16_bf16 with
 // fp32 accumulation.  Tile order as in gemm.hip (XCD-aware, grouped rows).
+// The B fragment is the MFMA's first operand, so the accumulators hold C^T
+// blocks: a lane owns one row of C and runs of 4 consecutive columns, which
+// the epilogues store (and the backward activations load) 8 bytes at a time.
 #include "common.h"
 #include "gemm.h"
 #include "gemm_common.h"
@@ -284,8 +287,8 @@ __device__ __forceinline__ void mma_stage(const char* ta_p, const char* tb_p, in
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[s & 1][i]),
-                                                            __builtin_bit_cast(bf16x8, bfr[s & 1][j]),
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfr[s & 1][j]),
+                                                            __builtin_bit_cast(bf16x8, af[s & 1][i]),
                                                             acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     // work slotted between the steps (the next stage's global->LDS loads):
@@ -371,8 +374,8 @@ __device__ __forceinline__ void mma_frags(const StageFrags<FM, FN, BK>& f, f32x1
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[s][i]),
-                                                            __builtin_bit_cast(bf16x8, f.b[s][j]), acc[i][j], 0,
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[s][j]),
+                                                            __builtin_bit_cast(bf16x8, f.a[s][i]), acc[i][j], 0,
                                                             0, 0);
 }
 
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
     k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
   }
 
-  rows_epilogue<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
+  rows_epilogue_t<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
     k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
   }
 
-  wgrad_epilogue<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+  wgrad_epilogue_t<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -638,14 +641,19 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile configurations (BM, BN, WM, WN, BK, NS, NP), chosen per launch kind
-// from measurements of the Mixtral-sized expert GEMMs (d 4096, F 14336):
+// Tile configurations (BM, BN, WM, WN, BK, NS, NP), from measurements of the
+// Mixtral-sized expert GEMMs (d 4096, F 14336):
 //  * CFG_PP: 256x256 tile, 8 waves in two ping-pong groups, K-step 32,
-//    4-stage ring: every row-split kind (forward, dgrad).
-//  * CFG_WIDE: the same tile with all 8 waves in lockstep: wgrad, whose
-//    operands both need transposing reads.
+//    4-stage ring: forward, plain dgrad and wgrad launches.
+//  * CFG_ACT_BWD: 256x128 tile, 4 MFMA waves fed by 4 load-only waves, K-step
+//    64, 3-stage ring: the SwiGLU dgrad launch, whose epilogue reads the saved
+//    gate and up activations (34% against 32% for CFG_PP on the Mixtral
+//    shape; the GELU' launches of the smaller workloads measured faster with
+//    CFG_PP).
+// (All 8 waves in lockstep and 4-wave 256x256 tiles measured slower for
+// every kind.)
 #define MOE_GEMM3_CFG_PP 256, 256, 2, 4, 32, 4, -1
-#define MOE_GEMM3_CFG_WIDE 256, 256, 2, 4, 32, 4, 0
+#define MOE_GEMM3_CFG_ACT_BWD 256, 128, 2, 2, 64, 3, 4
 
 // Whether the direct-load kernels take this launch: the K split of the SwiGLU
 // dgrad (gate | up weights) must fall on a stage boundary.
@@ -663,7 +671,7 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
     switch (epi) {
       case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
       case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
-      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_ACT_BWD, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   }
   return hipErrorInvalidValue;
@@ -671,8 +679,8 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
 
 hipError_t run_wgrad_bf16(int epi, const Args& a, hipStream_t st) {
   using namespace gemm;
-  if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG_WIDE, EPI_STORE>(a, st);
-  if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG_WIDE, EPI_STORE_SPLITN>(a, st);
+  if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG_PP, EPI_STORE>(a, st);
+  if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG_PP, EPI_STORE_SPLITN>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -209,5 +209,197 @@ __device__ __forceinline__ void wgrad_epilogue(const gemm::Args& a, f32x16 (&acc
     }
 }
 
+// ---------------------------------------------------------------------------
+// Epilogues for accumulators holding C^T blocks (the MFMA called with the
+// B fragment first): lane l holds row (l % 32) of a 32x32 block of C and,
+// for e = 4g + q, column 8g + 4(l / 32) + q.  So every lane owns four runs of
+// 4 consecutive columns of one row, stored (and, for the backward
+// activation, loaded) 8 bytes at a time.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tacc_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
+
+template <typename T> struct Run4;
+template <> struct Run4<bf16> {
+  typedef u32x2 Raw;  // the 4 elements as stored
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return *reinterpret_cast<const u32x2*>(p); }
+  static __device__ __forceinline__ void unpack(const Raw& w, float (&v)[4]) {
+    v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xffff0000u);
+    v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void load(const bf16* p, float (&v)[4]) { unpack(load_raw(p), v); }
+  static __device__ __forceinline__ void store(bf16* p, const float (&v)[4]) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                                         bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+  }
+};
+template <> struct Run4<float> {
+  typedef f32x4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ void unpack(const Raw& w, float (&v)[4]) {
+    v[0] = w[0]; v[1] = w[1]; v[2] = w[2]; v[3] = w[3];
+  }
+  static __device__ __forceinline__ void load(const float* p, float (&v)[4]) { unpack(load_raw(p), v); }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
+
+// Row-split kernels; N and every leading dimension are multiples of 8, so a
+// run of 4 columns starting at a multiple of 4 is all in range or all out.
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void rows_epilogue_t_bwd(const gemm::Args& a, f32x16 (&acc)[FM][FN],
+                                                    const int (&bcol)[FN], int wm0, int lane, int64_t row_begin,
+                                                    int64_t row_end, int64_t n0, int64_t N);
+
+template <typename T, int FM, int FN, bool PAIR, int EPI>
+__device__ __forceinline__ void rows_epilogue_t(const gemm::Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                                int wm0, int lane, int64_t row_begin, int64_t row_end, int64_t n0,
+                                                int64_t N) {
+  if constexpr (EPI == gemm::EPI_GELU_BWD || EPI == gemm::EPI_SWIGLU_BWD) {
+    rows_epilogue_t_bwd<T, FM, FN, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
+    return;
+  }
+  T* C = reinterpret_cast<T*>(a.C);
+  T* C2 = reinterpret_cast<T*>(a.C2);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t rr = row_begin + wm0 + i * 32 + (lane & 31);
+    if (rr >= row_end) continue;
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t f = n0 + bcol[j] + tacc_col(g, lane);
+          if (f >= N) continue;
+          float av[4], bv[4], hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            av[q] = acc[i][j][4 * g + q];
+            bv[q] = acc[i][j + FN / 2][4 * g + q];
+            hv[q] = av[q] * sigmoid_f(av[q]) * bv[q];
+          }
+          Run4<T>::store(C + rr * a.ldc + f, av);
+          Run4<T>::store(C + rr * a.ldc + a.c_split + f, bv);
+          Run4<T>::store(C2 + rr * a.ldc2 + f, hv);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + bcol[j] + tacc_col(g, lane);
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+          if constexpr (EPI == gemm::EPI_STORE) {
+            Run4<T>::store(C + rr * a.ldc + n, v);
+          } else if constexpr (EPI == gemm::EPI_GELU_FWD) {
+            float h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
+            Run4<T>::store(C + rr * a.ldc + n, v);
+            Run4<T>::store(C2 + rr * a.ldc2 + n, h);
+          }
+        }
+    }
+  }
+}
+
+// The backward activations read X1 (Z, or A | B).  Each lane's loads of one
+// 32-row block (FN x 4 runs, two per run for SwiGLU) are issued together and
+// one block ahead of the arithmetic; they are unconditional, from the tile's
+// first row / column when the run is out of range, and only the stores are
+// predicated, so no branch forces a wait on a single load.
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void rows_epilogue_t_bwd(const gemm::Args& a, f32x16 (&acc)[FM][FN],
+                                                    const int (&bcol)[FN], int wm0, int lane, int64_t row_begin,
+                                                    int64_t row_end, int64_t n0, int64_t N) {
+  constexpr bool SW = EPI == gemm::EPI_SWIGLU_BWD;
+  constexpr int NL = SW ? 2 : 1;
+  T* C = reinterpret_cast<T*>(a.C);
+  const T* X1 = reinterpret_cast<const T*>(a.X1);
+  typedef typename Run4<T>::Raw Raw;
+  Raw xin[2][FN][4][NL];  // two 32-row blocks of raw inputs
+  auto load_block = [&](int i, Raw (&dst)[FN][4][NL]) {
+    const int64_t rr = row_begin + wm0 + i * 32 + (lane & 31);
+    const int64_t r = rr < row_end ? rr : row_begin;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t nn = n0 + bcol[j] + tacc_col(g, lane);
+        const int64_t n = nn < N ? nn : n0;
+#pragma unroll
+        for (int h = 0; h < NL; ++h) dst[j][g][h] = Run4<T>::load_raw(X1 + r * a.ldx + h * a.c_split + n);
+      }
+  };
+  load_block(0, xin[0]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (i + 1 < FM) load_block(i + 1, xin[(i + 1) & 1]);
+    const int64_t rr = row_begin + wm0 + i * 32 + (lane & 31);
+    const bool row_ok = rr < row_end;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + bcol[j] + tacc_col(g, lane);
+        float x0[4];
+        Run4<T>::unpack(xin[i & 1][j][g][0], x0);
+        if constexpr (SW) {
+          float x1[4];
+          Run4<T>::unpack(xin[i & 1][j][g][NL - 1], x1);
+          float da[4], db[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float v = acc[i][j][4 * g + q], av = x0[q], bv = x1[q];
+            const float sg = sigmoid_f(av);
+            da[q] = v * bv * sg * (1.0f + av * (1.0f - sg));
+            db[q] = v * av * sg;
+          }
+          if (row_ok && n < N) {
+            Run4<T>::store(C + rr * a.ldc + n, da);
+            Run4<T>::store(C + rr * a.ldc + a.c_split + n, db);
+          }
+        } else {
+          float dz[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dz[q] = acc[i][j][4 * g + q] * gelu_grad_f(x0[q]);
+          if (row_ok && n < N) Run4<T>::store(C + rr * a.ldc + n, dz);
+        }
+      }
+  }
+}
+
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void wgrad_epilogue_t(const gemm::Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                                 int wm0, int lane, int wi, int64_t m0, int64_t n0, int64_t M,
+                                                 int64_t N) {
+  T* C = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride;
+  T* C2 = a.C2 ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride : nullptr;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm0 + i * 32 + (lane & 31);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + bcol[j] + tacc_col(g, lane);
+        if (n >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+        // c_split is a multiple of 8: a run never straddles it
+        if (EPI == gemm::EPI_STORE_SPLITN && n >= a.c_split)
+          Run4<T>::store(C2 + m * a.ldc + (n - a.c_split), v);
+        else
+          Run4<T>::store(C + m * a.ldc + n, v);
+      }
+  }
+}
+
 }  // namespace gemm_common
 }  // namespace moe
