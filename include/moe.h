@@ -121,10 +121,14 @@ int moe_plan(const moe_config* cfg, moe_sizes* out);
  *   logits [T, E] fp32: l = x W_r + b, fp32 accumulation.
  *   topk_idx [T, k] int32: per token, experts ordered by (logit descending,
  *   index ascending), first k — equal logits go to the lower index.
- *   topk_w [T, k] fp32: gate weights per cfg->gating. */
+ *   topk_w [T, k] fp32: gate weights per cfg->gating.
+ *   ws: caller workspace of moe_plan's workspace_bytes, 16-byte aligned;
+ *   required for bf16 (the call writes a re-packed copy of w_router there),
+ *   may be NULL for fp32.
+ * Errors: MOE_ERR_INVALID for a null required pointer or a misaligned x / ws. */
 int moe_route(const moe_config* cfg, const void* x, const void* w_router,
               const float* bias, float* logits, int32_t* topk_idx,
-              float* topk_w, void* stream);
+              float* topk_w, void* ws, void* stream);
 
 /* Capacity, counts, offsets, EP send layout and permutation (tutorial:
  * All-to-All 二/六, send sets S_ik of variable size; Piper 方法论 1:

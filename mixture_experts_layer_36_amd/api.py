@@ -35,9 +35,9 @@ def groups(n_groups: int, ffn: int, rows_max: int, offsets: torch.Tensor, use_pl
                      use_placement=1 if use_placement else 0)
 
 
-def moe_route(cfg, x, w_router, bias, logits, topk_idx, topk_w, stream=None):
+def moe_route(cfg, x, w_router, bias, logits, topk_idx, topk_w, ws, stream=None):
     call("moe_route", ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
-         _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+         _ptr(topk_idx), _ptr(topk_w), _ptr(ws), _stream(stream))
 
 
 def moe_dispatch(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts,

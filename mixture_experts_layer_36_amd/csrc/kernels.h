@@ -8,7 +8,8 @@ namespace moe {
 constexpr int kDispatchBlock = 256;  // tokens per block of the stable-rank kernels
 
 struct RouteArgs {
-  const void* x; const void* w; const float* bias;
+  const void* x; const void* w; uint32_t* wpack;  // wpack: workspace, bf16 weight pairs
+  const float* bias;
   float* logits; int32_t* topk_idx; float* topk_w;
   int64_t T; int d; int E; int k; int gating;
 };

@@ -51,7 +51,7 @@ int64_t capacity_of(const moe_config* c) {
 size_t elem_bytes(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 struct WsLayout {
-  size_t dispatch, route_bwd, ffn_routed, ffn_shared, total;
+  size_t dispatch, route, route_bwd, ffn_routed, ffn_shared, total;
 };
 
 WsLayout ws_layout(const moe_config* c, int64_t n_max) {
@@ -62,7 +62,9 @@ WsLayout ws_layout(const moe_config* c, int64_t n_max) {
   const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
   w.ffn_routed = round_up((size_t)n_max * m * c->ffn * elem_bytes(c), 256);
   w.ffn_shared = c->n_shared > 0 ? round_up((size_t)c->T * m * c->n_shared * c->ffn_shared * elem_bytes(c), 256) : 0;
+  w.route = c->dtype == MOE_BF16 ? round_up((size_t)c->d * c->E * 2, 256) : 0;
   w.total = w.dispatch;
+  if (w.route > w.total) w.total = w.route;
   if (w.route_bwd > w.total) w.total = w.route_bwd;
   if (w.ffn_routed > w.total) w.total = w.ffn_routed;
   if (w.ffn_shared > w.total) w.total = w.ffn_shared;
@@ -177,13 +179,14 @@ int moe_plan(const moe_config* cfg, moe_sizes* out) {
 }
 
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias, float* logits,
-              int32_t* topk_idx, float* topk_w, void* stream) {
+              int32_t* topk_idx, float* topk_w, void* ws, void* stream) {
   int s = check_config(cfg);
   if (s != MOE_OK) return s;
   if (!x || !w_router || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID;
-  if (!aligned16(x)) return MOE_ERR_INVALID;
-  moe::RouteArgs a{x, w_router, bias, logits, topk_idx, topk_w, cfg->T, (int)cfg->d, (int)cfg->E, (int)cfg->k,
-                   cfg->gating};
+  if (cfg->dtype == MOE_BF16 && !ws) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(ws)) return MOE_ERR_INVALID;
+  moe::RouteArgs a{x, w_router, (uint32_t*)ws, bias, logits, topk_idx, topk_w, cfg->T, (int)cfg->d, (int)cfg->E,
+                   (int)cfg->k, cfg->gating};
   return hip_status(moe::launch_route(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
 }
 

@@ -12,7 +12,8 @@
 // every lane, so they come in through wave-uniform scalar loads and feed the
 // dot products straight from scalar registers: bf16 uses the two-term
 // fp32-accumulating dot instruction on (x[k], x[k+1]) . (W[k][e], W[k+1][e]),
-// fp32 plain FMAs.  The W per-wave partial logits are then summed in a fixed
+// with the weight pairs packed once per call into a workspace copy so that
+// each pair is one scalar dword; fp32 uses plain FMAs on W itself.  The W per-wave partial logits are then summed in a fixed
 // binary tree through LDS, so the logits are deterministic.  Lane t of wave 0
 // finally holds all logits of its token and does the softmax statistics and
 // the k rounds of arg-max sequentially, ordering by (logit descending, expert
@@ -36,37 +37,15 @@ template <int EP> constexpr size_t route_lds() {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-// 16-bit packs (lo(a), lo(b)) and (hi(a), hi(b)) of wave-uniform operands.
-// The first is selected as the scalar pack instruction from a vector build;
-// the second has no such pattern, so it is written out.
-__device__ __forceinline__ uint32_t s_pack_ll(uint32_t a, uint32_t b) {
-  const u16x2_t v = {(unsigned short)a, (unsigned short)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ uint32_t s_pack_hh(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
-  return r;
-}
-
-// Router weight pair (W[k][e], W[k+1][e]) as one dword of two bf16: rows are
-// E elements long, so the pair is gathered from two rows with scalar loads.
-// With E even and k even both rows start on a dword, and the pair is one
-// scalar pack of the dwords holding experts (e & ~1, e | 1) of rows k, k+1.
+// Router weight pair (W[k][e], W[k+1][e]) for even k, from the packed copy
+// wp[k/2][e] (one dword of two bf16) that pack_router_pairs_kernel writes.
 template <int EP, bool FULL>
-__device__ __forceinline__ uint32_t w_pair(const uint32_t* __restrict__ wd, int k, int e, int E) {
+__device__ __forceinline__ uint32_t w_pair(const uint32_t* __restrict__ wp, int k, int e, int E) {
   if constexpr (FULL) {
-    const uint32_t d0 = wd[(k * EP + e) >> 1], d1 = wd[((k + 1) * EP + e) >> 1];
-    return (e & 1) ? s_pack_hh(d0, d1) : s_pack_ll(d0, d1);
+    return wp[(k >> 1) * EP + e];
   } else {
-    const int ee = e < E ? e : E - 1;
-    const int i0 = k * E + ee, i1 = i0 + E;
-    const uint32_t d0 = wd[i0 >> 1], d1 = wd[i1 >> 1];
-    const uint32_t lo = (i0 & 1) ? (d0 >> 16) : (d0 & 0xffffu);
-    const uint32_t hi = (i1 & 1) ? (d1 >> 16) : (d1 & 0xffffu);
-    return e < E ? (lo | (hi << 16)) : 0u;
+    const uint32_t v = wp[(k >> 1) * E + (e < E ? e : E - 1)];
+    return e < E ? v : 0u;
   }
 }
 
@@ -78,10 +57,103 @@ __device__ __forceinline__ float w_f32(const float* __restrict__ w, int k, int e
   return (FULL || e < E) ? v : 0.0f;
 }
 
+// Software-pipelined bf16 path for E equal to its padded width.  The packed
+// weight pairs of one 16-byte piece of x (4 pairs x EP experts) are fetched in
+// 32-dword units (an even number per piece, pairs-major) into two alternating
+// scalar-register buffers.  Scalar loads return out of order, so a step first
+// waits for everything outstanding, then issues the next unit's loads and,
+// at a piece's first unit, the LDS read of the next piece, and only then
+// computes from the unit that has already arrived.
+template <int EP>
+struct PairUnit {
+  static constexpr int DW = 32;                       // dwords per unit
+  static constexpr int EPU = EP < DW ? EP : DW;       // experts per unit
+  static constexpr int PPU = DW / EPU;                // pairs per unit
+  static constexpr int UPP = 4 / PPU * (EP / EPU);    // units per piece
+};
+
+__device__ __forceinline__ void wait_lgkm_all() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int EP>
+__device__ __forceinline__ void load_unit(const uint32_t* __restrict__ wp, int k0, int v,
+                                          uint32_t (&b)[PairUnit<EP>::DW]) {
+  using U = PairUnit<EP>;
+  constexpr int EG = EP / U::EPU;
+  const int pq = v / EG, eg = v % EG;
+#pragma unroll
+  for (int p = 0; p < U::PPU; ++p) {
+    const uint32_t* row = wp + ((k0 >> 1) + pq * U::PPU + p) * EP + eg * U::EPU;
+#pragma unroll
+    for (int i = 0; i < U::EPU; ++i) b[p * U::EPU + i] = row[i];
+  }
+}
+
+template <int EP>
+__device__ __forceinline__ void compute_unit(const u32x4& xj, int v, const uint32_t (&b)[PairUnit<EP>::DW],
+                                             float (&acc)[EP]) {
+  using U = PairUnit<EP>;
+  constexpr int EG = EP / U::EPU;
+  const int pq = v / EG, eg = v % EG;
+#pragma unroll
+  for (int p = 0; p < U::PPU; ++p) {
+    // through a scalar: this compiler's bit_cast of a vector element
+    // expression reads element 0 whatever the index
+    const uint32_t xu = xj[pq * U::PPU + p];
+    const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xu);
+#pragma unroll
+    for (int i = 0; i < U::EPU; ++i) {
+      const int e = eg * U::EPU + i;
+      acc[e] = __builtin_amdgcn_fdot2_f32_bf16(xp, __builtin_bit_cast(bf16x2_t, b[p * U::EPU + i]), acc[e], false);
+    }
+  }
+}
+
+// All pieces of one chunk; piece j of the lane's row is at slot j ^ (lane % 8)
+// of its 128-byte LDS row.  Past the last piece the prefetches repeat the last
+// one (in range, unused), which keeps them unconditional.
+template <int EP>
+__device__ __forceinline__ void chunk_pipelined(const uint32_t* __restrict__ wp, const char* lrow, int lane, int kb,
+                                                int npiece, float (&acc)[EP]) {
+  using U = PairUnit<EP>;
+  static_assert(U::UPP % 2 == 0, "buffers alternate within a piece");
+  uint32_t wa[U::DW], wb[U::DW];
+  u32x4 xcur = ld16(lrow + ((0 ^ (lane & 7)) << 4)), xnext = xcur;
+  load_unit<EP>(wp, kb, 0, wa);
+  for (int j = 0; j < npiece; ++j) {
+    const int k0 = kb + 8 * j;
+    const int jn = min(j + 1, npiece - 1);
+#pragma unroll
+    for (int v = 0; v < U::UPP; ++v) {
+      wait_lgkm_all();
+      __builtin_amdgcn_sched_barrier(0);
+      // next unit: (j, v + 1), or (jn, 0) after the piece's last unit
+      if (v + 1 < U::UPP) load_unit<EP>(wp, k0, v + 1, (v & 1) ? wa : wb);
+      else load_unit<EP>(wp, kb + 8 * jn, 0, (v & 1) ? wa : wb);
+      if (v == 0) xnext = ld16(lrow + ((jn ^ (lane & 7)) << 4));
+      __builtin_amdgcn_sched_barrier(0);
+      compute_unit<EP>(xcur, v, (v & 1) ? wb : wa, acc);
+    }
+    xcur = xnext;
+  }
+}
+
 }  // namespace
+
+// wp[k/2][e] = W[k][e] | W[k+1][e] << 16 for even k (d is even).
+__global__ __launch_bounds__(256) void pack_router_pairs_kernel(const uint16_t* __restrict__ w,
+                                                                uint32_t* __restrict__ wp, int d, int E) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)(d / 2) * E;
+  if (i >= n) return;
+  const int64_t kp = i / E, e = i - kp * E;
+  wp[i] = (uint32_t)w[2 * kp * E + e] | ((uint32_t)w[(2 * kp + 1) * E + e] << 16);
+}
 
 template <typename T, int EP, bool FULL>
 __global__ __launch_bounds__(route_waves<EP>() * 64) void route_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                                       const uint32_t* __restrict__ wpack,
                                                                 const float* __restrict__ bias,
                                                                 float* __restrict__ logits,
                                                                 int32_t* __restrict__ topk_idx,
@@ -137,11 +209,16 @@ __global__ __launch_bounds__(route_waves<EP>() * 64) void route_kernel(const T* 
     // that every register index is static.
     const int kb = c * KC;
     const int npiece = min(KC, d - kb) / (16 / (int)sizeof(T));  // d is a multiple of 8
+    // pipelined weight units for E >= 16; with 8 experts a piece's weights
+    // are only 32 dwords and the plain loop measured faster
+    if constexpr (FULL && sizeof(T) == 2 && EP >= 16) {
+      chunk_pipelined<EP>(wpack, stage + lane * 128, lane, kb, npiece, acc);
+    } else {
 #pragma unroll 2
     for (int j = 0; j < npiece; ++j) {
       const u32x4 xj = ld16(stage + lane * 128 + ((j ^ (lane & 7)) << 4));
       if constexpr (sizeof(T) == 2) {
-        const uint32_t* wd = reinterpret_cast<const uint32_t*>(w);
+        const uint32_t* wd = wpack;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int kk = kb + 8 * j + 2 * q;
@@ -168,6 +245,7 @@ __global__ __launch_bounds__(route_waves<EP>() * 64) void route_kernel(const T* 
           if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
         }
       }
+    }
     }
     // the next chunk's LDS writes stay behind this chunk's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -275,8 +353,16 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
       reinterpret_cast<const void*>(route_kernel<T, EP, false>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (prep_full != hipSuccess) return prep_full;
   if (prep_part != hipSuccess) return prep_part;
+  if constexpr (sizeof(T) == 2) {
+    const int64_t n = (int64_t)(a.d / 2) * a.E;
+    hipLaunchKernelGGL(pack_router_pairs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)a.w, a.wpack, a.d, a.E);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(route_waves<EP>() * 64), lds, st, (const T*)a.x,
-                     (const T*)a.w, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k, a.gating);
+                     (const T*)a.w, a.wpack, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k,
+                     a.gating);
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ class MoELayer:
 
     # ------------------------------------------------------------------ steps
     def route(self, x, w: Weights):
-        api.moe_route(self.cfg, x, w.w_router, w.bias, self.logits, self.topk_idx, self.topk_w)
+        api.moe_route(self.cfg, x, w.w_router, w.bias, self.logits, self.topk_idx, self.topk_w, self.ws)
 
     def dispatch(self, x):
         api.moe_dispatch(self.cfg, x, self.topk_idx, self.x_perm, self.row_of, self.assign_of_row,

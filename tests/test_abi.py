@@ -104,7 +104,7 @@ def test_null_pointers_rejected_before_launch(lib):
     N = None
     assert lib.moe_plan(cp, N) == nat.MOE_ERR_INVALID
     assert lib.moe_plan(N, N) == nat.MOE_ERR_INVALID
-    assert lib.moe_route(cp, N, N, N, N, N, N, N) == nat.MOE_ERR_INVALID
+    assert lib.moe_route(cp, N, N, N, N, N, N, N, N) == nat.MOE_ERR_INVALID
     assert lib.moe_dispatch(cp, *([N] * 12)) == nat.MOE_ERR_INVALID
     g = nat.MoeGroups(groups=8, ffn=64, rows_max=128, offsets=None, use_placement=1)
     assert lib.moe_expert_ffn_fwd(cp, ctypes.byref(g), *([N] * 8)) == nat.MOE_ERR_INVALID
@@ -128,7 +128,9 @@ def test_bad_groups_and_alignment_rejected(lib):
         assert st in (nat.MOE_ERR_INVALID, nat.MOE_ERR_UNSUPPORTED)
     g = nat.MoeGroups(groups=8, ffn=64, rows_max=128, offsets=fake, use_placement=1)
     assert lib.moe_expert_ffn_fwd(cp, ctypes.byref(g), odd, *([fake] * 6), None) == nat.MOE_ERR_INVALID
-    assert lib.moe_route(cp, odd, fake, None, fake, fake, fake, None) == nat.MOE_ERR_INVALID
+    assert lib.moe_route(cp, odd, fake, None, fake, fake, fake, fake, None) == nat.MOE_ERR_INVALID
+    assert lib.moe_route(cp, fake, fake, None, fake, fake, fake, odd, None) == nat.MOE_ERR_INVALID
+    assert lib.moe_route(cp, fake, fake, None, fake, fake, fake, None, None) == nat.MOE_ERR_INVALID  # bf16 needs ws
     assert lib.moe_combine(cp, odd, fake, fake, None, fake, None) == nat.MOE_ERR_INVALID
 
 

@@ -81,6 +81,22 @@ FUZZ = {
     "T2000_E5_f32_shared": W("T2000_E5_f32_shared", T=2000, d=40, ffn=48, E=5, k=2, capacity_factor=1.1,
                              gating="softmax_topk", act="swiglu", dtype="f32", n_shared=1,
                              ffn_shared=16, seed=20),
+    # every expert-count specialisation of the routing / router-backward /
+    # un-permute kernels: E equal to its padded width (8, 16, 32, 64) and E
+    # below it, for both dtypes, with top-k at most 2 and above 2
+    "T129_E32_bf16": W("T129_E32_bf16", T=129, d=136, ffn=72, E=32, k=3, capacity_factor=1.2,
+                       gating="softmax_topk", act="gelu", dtype="bf16", seed=21),
+    "T200_E8_f32": W("T200_E8_f32", T=200, d=64, ffn=32, E=8, k=2, capacity_factor=1.0,
+                     gating="topk_softmax", act="swiglu", dtype="f32", seed=22),
+    "T96_E16_f32": W("T96_E16_f32", T=96, d=48, ffn=40, E=16, k=4, capacity_factor=0.0,
+                     gating="softmax_topk_renorm", act="gelu", dtype="f32", seed=23),
+    "T150_E12_bf16": W("T150_E12_bf16", T=150, d=80, ffn=56, E=12, k=2, capacity_factor=1.5,
+                       gating="softmax_topk", act="swiglu", dtype="bf16", seed=24),
+    "T90_E40_bf16": W("T90_E40_bf16", T=90, d=48, ffn=24, E=40, k=4, capacity_factor=0.0,
+                      gating="topk_softmax", act="swiglu", dtype="bf16", ep_ranks=8, seed=25),
+    "T70_E20_f32": W("T70_E20_f32", T=70, d=56, ffn=32, E=20, k=1, capacity_factor=2.0,
+                     gating="softmax_topk", act="gelu", dtype="f32", ep_ranks=4, placement="round_robin",
+                     seed=26),
 }
 
 
