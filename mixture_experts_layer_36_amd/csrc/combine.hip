@@ -17,16 +17,22 @@ namespace moe {
 // (U chunks of each of the <= KMAX gathered rows) before it combines them.
 constexpr int kRowWaves = 4;  // waves (tokens) per workgroup
 
-template <int KMAX> constexpr int row_unroll() { return KMAX <= 2 ? 4 : 2; }
+// Chunks per lane per round: enough for one round per row on wide rows,
+// fewer where most lanes would have nothing to load.
+inline int row_unroll(int64_t d, int elem_bytes, int kmax) {
+  const int64_t nch = d * elem_bytes / 16;
+  if (kmax > 2) return 2;
+  return nch > 256 ? 8 : nch > 128 ? 4 : 2;
+}
 
 // y[t] = sum_j g[t,j] * y_perm[row_of[t,j]] (+ y_shared[t])
-template <typename T, int KMAX>
+template <typename T, int KMAX, int U>
 __global__ __launch_bounds__(64 * kRowWaves) void combine_kernel(const T* __restrict__ y_perm,
                                                                  const int32_t* __restrict__ row_of,
                                                                  const float* __restrict__ topk_w,
                                                                  const T* __restrict__ y_shared, T* __restrict__ y,
                                                                  int64_t Tn, int d, int k) {
-  constexpr int V = Vec16<T>::N, U = row_unroll<KMAX>();
+  constexpr int V = Vec16<T>::N;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void combine_kernel(const T* __rest
 }
 
 // dy_perm[row] = g * dy[t]; d_topk_w[t,j] = <dy[t], y_perm[row]>, one wave per token.
-template <typename T, int KMAX>
+template <typename T, int KMAX, int U>
 __global__ __launch_bounds__(64 * kRowWaves) void combine_bwd_kernel(const T* __restrict__ dy,
                                                                      const T* __restrict__ y_perm,
                                                                      const int32_t* __restrict__ row_of,
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void combine_bwd_kernel(const T* __
                                                                      T* __restrict__ dy_perm,
                                                                      float* __restrict__ d_topk_w, int64_t Tn, int d,
                                                                      int k) {
-  constexpr int V = Vec16<T>::N, U = row_unroll<KMAX>();
+  constexpr int V = Vec16<T>::N;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -274,15 +280,15 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
   }
 }
 
-template <typename T, int KMAX>
-static hipError_t launch_combine_t(const CombineArgs& a, bool backward, hipStream_t st) {
+template <typename T, int KMAX, int U>
+static hipError_t launch_combine_u(const CombineArgs& a, bool backward, hipStream_t st) {
   const int64_t blocks = (a.T + kRowWaves - 1) / kRowWaves;
   if (blocks <= 0) return hipSuccess;
   if (!backward)
-    hipLaunchKernelGGL((combine_kernel<T, KMAX>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
+    hipLaunchKernelGGL((combine_kernel<T, KMAX, U>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
                        (const T*)a.y_perm, a.row_of, a.topk_w, (const T*)a.y_shared, (T*)a.y, a.T, (int)a.d, a.k);
   else
-    hipLaunchKernelGGL((combine_bwd_kernel<T, KMAX>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
+    hipLaunchKernelGGL((combine_bwd_kernel<T, KMAX, U>), dim3((unsigned)blocks), dim3(64 * kRowWaves), 0, st,
                        (const T*)a.dy, (const T*)a.y_perm, a.row_of, a.topk_w, (T*)a.dy_perm, a.d_topk_w, a.T,
                        (int)a.d, a.k);
   return hipGetLastError();
@@ -290,7 +296,12 @@ static hipError_t launch_combine_t(const CombineArgs& a, bool backward, hipStrea
 
 template <typename T>
 static hipError_t launch_combine_dt(const CombineArgs& a, bool backward, hipStream_t st) {
-  return a.k <= 2 ? launch_combine_t<T, 2>(a, backward, st) : launch_combine_t<T, 8>(a, backward, st);
+  if (a.k > 2) return launch_combine_u<T, 8, 2>(a, backward, st);
+  switch (row_unroll(a.d, sizeof(T), a.k)) {
+    case 8: return launch_combine_u<T, 2, 8>(a, backward, st);
+    case 4: return launch_combine_u<T, 2, 4>(a, backward, st);
+    default: return launch_combine_u<T, 2, 2>(a, backward, st);
+  }
 }
 
 hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st) {

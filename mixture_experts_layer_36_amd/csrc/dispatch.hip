@@ -132,15 +132,16 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
 
 // One wave per token: its kept rows (wave-uniform scalar loads) receive the
 // token's row; each lane moves the 16-byte chunks lane, lane + 64, ... of it,
-// U at a time, with the U loads issued before the stores.
+// U at a time (2, 4 or 8 by row width), with the U loads issued before the
+// stores.
 constexpr int kCopyWaves = 4;
 
-template <typename T, int KMAX>
+template <typename T, int KMAX, int U>
 __global__ __launch_bounds__(64 * kCopyWaves) void permute_copy_kernel(const T* __restrict__ x,
                                                                        const int32_t* __restrict__ row_of,
                                                                        T* __restrict__ x_perm, int64_t Tn, int d,
                                                                        int k) {
-  constexpr int V = Vec16<T>::N, U = 4;
+  constexpr int V = Vec16<T>::N;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kCopyWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -172,16 +173,29 @@ __global__ __launch_bounds__(64 * kCopyWaves) void permute_copy_kernel(const T* 
   }
 }
 
-template <typename T>
-static void launch_permute_copy(const DispatchArgs& a, hipStream_t st) {
+template <typename T, int KMAX>
+static void launch_permute_copy_k(const DispatchArgs& a, hipStream_t st) {
   const int64_t blocks = (a.T + kCopyWaves - 1) / kCopyWaves;
   if (blocks <= 0) return;
-  if (a.k <= 2)
-    hipLaunchKernelGGL((permute_copy_kernel<T, 2>), dim3((unsigned)blocks), dim3(64 * kCopyWaves), 0, st,
-                       (const T*)a.x, a.row_of, (T*)a.x_perm, a.T, (int)a.d, a.k);
+  // chunks per lane per round: one round per row on wide rows, fewer where
+  // most lanes would have nothing to move
+  const int64_t nch = a.d * (int64_t)sizeof(T) / 16;
+  const dim3 grid((unsigned)blocks), block(64 * kCopyWaves);
+  if (nch > 256)
+    hipLaunchKernelGGL((permute_copy_kernel<T, KMAX, 8>), grid, block, 0, st, (const T*)a.x, a.row_of,
+                       (T*)a.x_perm, a.T, (int)a.d, a.k);
+  else if (nch > 128)
+    hipLaunchKernelGGL((permute_copy_kernel<T, KMAX, 4>), grid, block, 0, st, (const T*)a.x, a.row_of,
+                       (T*)a.x_perm, a.T, (int)a.d, a.k);
   else
-    hipLaunchKernelGGL((permute_copy_kernel<T, 8>), dim3((unsigned)blocks), dim3(64 * kCopyWaves), 0, st,
-                       (const T*)a.x, a.row_of, (T*)a.x_perm, a.T, (int)a.d, a.k);
+    hipLaunchKernelGGL((permute_copy_kernel<T, KMAX, 2>), grid, block, 0, st, (const T*)a.x, a.row_of,
+                       (T*)a.x_perm, a.T, (int)a.d, a.k);
+}
+
+template <typename T>
+static void launch_permute_copy(const DispatchArgs& a, hipStream_t st) {
+  if (a.k <= 2) launch_permute_copy_k<T, 2>(a, st);
+  else launch_permute_copy_k<T, 8>(a, st);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st) {

@@ -62,7 +62,7 @@ __device__ __forceinline__ void load_row_cols(const T* p, float (&v)[CPT]) {
 // partial[b][i][e] = sum over tokens t of token block b of x[t, i] * dl[t, e].
 // A lane owns CPT = 64 / EP consecutive columns (all EP experts: 64 fp32
 // accumulators); the 4 waves of a workgroup take consecutive quarters of the
-// block's tokens, 4 tokens per round with their x loads issued first, the
+// block's tokens, 8 tokens per round with their x loads issued first, the
 // tokens' dlogits coming in through wave-uniform scalar loads.  The waves'
 // sums are added in wave order through LDS, so the partials are deterministic.
 constexpr int kRwgWaves = 4;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_partial_kernel(co
                                                                               float* __restrict__ partial,
                                                                               int64_t Tn, int d, int E, int tw) {
   static_assert(CPT * EP == 64, "64 accumulators per lane");
-  constexpr int TU = 4;
+  constexpr int TU = 8;
   __shared__ float red[kRwgWaves - 1][64][64];  // [wave - 1][accumulator][lane]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -142,14 +142,34 @@ __global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_partial_kernel(co
   }
 }
 
+// dw[i] = sum over b in order of partial[b][i].  A thread owns 4 consecutive
+// outputs and loads all its partials (nb <= 64, 16-byte loads) before the
+// in-order sums, so the loads overlap instead of following one another.
 template <typename T>
 __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ partial, int nb,
                                                                   int64_t dE, T* __restrict__ dw) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= dE) return;
-  float s = 0.0f;
-  for (int b = 0; b < nb; ++b) s += partial[(int64_t)b * dE + i];
-  dw[i] = from_f32<T>(s);
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= dE) return;
+  if (i0 + 4 <= dE && (dE & 3) == 0) {
+    f32x4 v[64];
+#pragma unroll
+    for (int b = 0; b < 64; ++b)
+      if (b < nb) v[b] = *reinterpret_cast<const f32x4*>(partial + (int64_t)b * dE + i0);
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int b = 0; b < 64; ++b)
+      if (b < nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] += v[b][q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dw[i0 + q] = from_f32<T>(s[q]);
+  } else {
+    for (int64_t i = i0; i < i0 + 4 && i < dE; ++i) {
+      float s = 0.0f;
+      for (int b = 0; b < nb; ++b) s += partial[(int64_t)b * dE + i];
+      dw[i] = from_f32<T>(s);
+    }
+  }
 }
 
 template <typename T, int EP>
@@ -167,7 +187,7 @@ static hipError_t launch_rwg(const RouteBwdArgs& a, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t dE = a.d * a.E;
-  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
                      a.partial, nb, dE, (T*)a.dw_router);
   return hipGetLastError();
 }
