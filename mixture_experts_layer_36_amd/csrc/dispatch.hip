@@ -53,12 +53,24 @@ __global__ __launch_bounds__(64) void scan_kernel(const int32_t* __restrict__ bl
   __shared__ int64_t kept_s[64];
   const int e = threadIdx.x;
   if (e < E) {
+    // running sum down the expert's column of block counts, 16 blocks per
+    // round with their loads issued first
     int64_t run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i = (int64_t)b * E + e;
-      const int c = block_counts[i];
-      block_base[i] = (int32_t)run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        // clamped, unconditional load and a select: no branch per load
+        const int b = b0 + u < nb ? b0 + u : nb - 1;
+        const int v = block_counts[(int64_t)b * E + e];
+        c[u] = b0 + u < nb ? v : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u >= nb) break;
+        block_base[(int64_t)(b0 + u) * E + e] = (int32_t)run;
+        run += c[u];
+      }
     }
     raw_counts[e] = (int32_t)run;
     const int64_t kept = run < C ? run : C;

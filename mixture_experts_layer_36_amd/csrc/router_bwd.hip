@@ -3,7 +3,7 @@
 // gradients that are aggregated across replicas; here they are computed for
 // one GPU's tokens).
 //
-// gating_bwd: one wave per token, lane e holds expert e (E <= 64).
+// gating_bwd: lane e of a token's lane group holds expert e (E <= 64).
 //   SOFTMAX_TOPK:          dl = p * (dp - <p, dp>),  p = softmax(l), dp[e_j] = dg_j
 //   RENORM / TOPK_SOFTMAX: the weights are a softmax over the chosen logits:
 //                          dl[e_j] = g_j * (dg_j - sum_m g_m dg_m), 0 elsewhere
@@ -15,37 +15,52 @@
 
 namespace moe {
 
+// G lanes per token (G = E rounded up to a power of two, at least 8), 64 / G
+// tokens per wave; the softmax statistics and the weighted sums are
+// reductions over the token's G lanes.
+template <int G>
 __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict__ logits,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ dg, float* __restrict__ dl,
                                                          int64_t Tn, int E, int k, int gating) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= Tn) return;
-  const bool valid = lane < E;
-  const float l = valid ? logits[t * E + lane] : -INFINITY;
+  const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+  const int e = lane % G;
+  const bool tok = t < Tn;  // every lane stays for the group reductions
+  const bool valid = tok && e < E;
+  const float l = valid ? logits[t * E + e] : -INFINITY;
   int sel = -1;
   for (int j = 0; j < k; ++j)
-    if (idx[t * k + j] == lane) sel = j;
+    if (tok && idx[t * k + j] == e) sel = j;
   const float dgl = sel >= 0 ? dg[t * k + sel] : 0.0f;
   float out;
   if (gating == 0) {
-    const float mx = group_max<64>(l);
+    const float mx = group_max<G>(l);
     float p = valid ? __expf(l - mx) : 0.0f;
-    const float z = group_sum<64>(p);
-    p = p / z;
-    const float s = group_sum<64>(p * dgl);
+    const float z = group_sum<G>(p);
+    p = z > 0.0f ? p / z : 0.0f;
+    const float s = group_sum<G>(p * dgl);
     out = p * (dgl - s);
   } else {
     const float lsel = sel >= 0 ? l : -INFINITY;
-    const float mx = group_max<64>(lsel);
+    const float mx = group_max<G>(lsel);
     float q = sel >= 0 ? __expf(l - mx) : 0.0f;
-    const float z = group_sum<64>(q);
-    const float g = q / z;
-    const float s = group_sum<64>(g * dgl);
+    const float z = group_sum<G>(q);
+    const float g = z > 0.0f ? q / z : 0.0f;
+    const float s = group_sum<G>(g * dgl);
     out = sel >= 0 ? g * (dgl - s) : 0.0f;
   }
-  if (valid) dl[t * E + lane] = out;
+  if (valid) dl[t * E + e] = out;
+}
+
+template <int G>
+static hipError_t launch_gating_bwd(const RouteBwdArgs& a, hipStream_t st) {
+  constexpr int TPB = 4 * (64 / G);  // tokens per workgroup
+  const int64_t blocks = (a.T + TPB - 1) / TPB;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gating_bwd_kernel<G>), dim3((unsigned)blocks), dim3(256), 0, st, a.logits, a.topk_idx,
+                     a.d_topk_w, a.dlogits, a.T, a.E, a.k, a.gating);
+  return hipGetLastError();
 }
 
 // CPT consecutive elements of a row as floats (16, 8, 4 or 2 bytes).
@@ -208,10 +223,10 @@ int router_wgrad_blocks(int64_t T) {
 }
 
 hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t st) {
-  const int64_t blocks = (a.T + 3) / 4;
-  hipLaunchKernelGGL(gating_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.logits, a.topk_idx, a.d_topk_w,
-                     a.dlogits, a.T, a.E, a.k, a.gating);
-  hipError_t err = hipGetLastError();
+  hipError_t err = a.E <= 8 ? launch_gating_bwd<8>(a, st)
+                   : a.E <= 16 ? launch_gating_bwd<16>(a, st)
+                   : a.E <= 32 ? launch_gating_bwd<32>(a, st)
+                   : launch_gating_bwd<64>(a, st);
   if (err != hipSuccess) return err;
   return bf16_dtype ? launch_rwg_dt<bf16>(a, st) : launch_rwg_dt<float>(a, st);
 }
