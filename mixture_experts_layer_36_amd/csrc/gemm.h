@@ -33,6 +33,10 @@ struct Args {
   int rr_R = 0, rr_L = 1;   // round-robin slot -> expert map (rr_R = 0: identity)
   int tiles_m = 0, tiles_n = 0;
   int gm = 8;               // row tiles per ordering group (L2 reuse of column panels)
+  // WGRAD split over the reduction (bf16 only): ksplit > 1 launches write
+  // fp32 partials [ksplit][weight sets][M][N] to `partial`, then summed
+  float* partial = nullptr;
+  int ksplit = 1;
 };
 
 template <typename T>
@@ -45,6 +49,10 @@ hipError_t run_wgrad(int epi, const Args& a, hipStream_t st);
 // bf16 kernels with direct global -> LDS loads (gemm3.hip)
 namespace gemm3 {
 bool supports(const gemm::Args& a);
+// Reduction splits of a bf16 WGRAD launch over `groups` groups of at most
+// rows_max rows in total (a function of host-known sizes only, so that the
+// workspace can be sized for it): 1 unless the launch has too few tiles.
+int wgrad_ksplit(int64_t groups, int64_t M, int64_t N, int64_t rows_max);
 hipError_t run_rows_bf16(int kind, int epi, const gemm::Args& a, int64_t rows_max, hipStream_t st);
 hipError_t run_wgrad_bf16(int epi, const gemm::Args& a, hipStream_t st);
 }  // namespace gemm3

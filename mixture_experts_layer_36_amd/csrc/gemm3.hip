@@ -418,6 +418,9 @@ __device__ __forceinline__ void k_loop_pingpong(char* smem, int nk, int group, c
 }
 
 constexpr int kPingPong = -1;  // NP value selecting the ping-pong loop
+// WGRAD epilogue selector (internal) of a launch split over the reduction:
+// each split writes an fp32 partial [split][weight set][M][N], summed after
+constexpr int kEpiPartial = 100;
 
 // ---------------------------------------------------------------------------
 // FWD / DGRAD: rows split by group.  A = activation rows (K-contiguous).
@@ -538,14 +541,32 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
   constexpr int STAGE = A_BYTES + B_BYTES;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
+  // EPI_PARTIAL launches split the reduction: block `lin` takes split
+  // lin / (groups * tiles) and writes an fp32 partial
+  constexpr bool SPLIT = EPI == kEpiPartial;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = a.tiles_m * a.tiles_n;
-  const int g = lin / per_g;
+  int split = 0, t = lin;
+  if constexpr (SPLIT) {
+    split = lin / (per_g * a.groups);
+    t = lin - split * per_g * a.groups;
+    if (split >= a.ksplit) return;
+  }
+  const int g = t / per_g;
   if (g >= a.groups) return;
   int mt, nt;
-  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt, a.gm);
+  grouped_order(t - g * per_g, a.tiles_m, a.tiles_n, mt, nt, a.gm);
   const int wi = weight_index(g, a.rr_R, a.rr_L);
-  const int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
+  int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
+  if constexpr (SPLIT) {
+    // split s takes rows [r0 + s*chunk, r0 + (s+1)*chunk) of the group, chunk
+    // a multiple of BK; a split past the group's rows keeps an empty range
+    // and writes zeros
+    const int64_t chunk = ((r1 - r0 + a.ksplit - 1) / a.ksplit + BK - 1) / BK * BK;
+    const int64_t b = r0 + split * chunk;
+    r0 = b < r1 ? b : r1;
+    r1 = b + chunk < r1 ? b + chunk : r1;
+  }
   const int64_t Kr = r1 - r0;
   const int64_t M = a.M, N = a.N;
   const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
@@ -604,7 +625,41 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
     k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
   }
 
-  wgrad_epilogue_t<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+  if constexpr (SPLIT) {
+    // fp32 partial of this split: [split][weight set][M][N]
+    Args ap = a;
+    ap.C = a.partial + (int64_t)split * a.groups * M * N;
+    ap.C2 = nullptr;
+    ap.ldc = N;
+    ap.c_gstride = M * N;
+    wgrad_epilogue_t<float, FM, FN, gemm::EPI_STORE>(ap, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+  } else {
+    wgrad_epilogue_t<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+  }
+}
+
+// Sum of the ksplit fp32 partials of a split WGRAD launch, in split order,
+// into the weight gradient (columns >= c_split to C2 for EPI_STORE_SPLITN);
+// 4 consecutive columns per thread.
+__global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(Args a, int epi) {
+  const int64_t M = a.M, N = a.N, per = M * N;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // over groups x M x N
+  if (i >= (int64_t)a.groups * per) return;
+  const int64_t wi = i / per, r = i - wi * per, m = r / N, n = r - m * N;
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < a.ksplit; ++s) {
+    float p[4];
+    Run4<float>::load(a.partial + (int64_t)s * a.groups * per + i, p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += p[q];
+  }
+  bf16* C = reinterpret_cast<bf16*>(a.C) + wi * a.c_gstride;
+  if (epi == gemm::EPI_STORE_SPLITN && n >= a.c_split) {
+    bf16* C2 = reinterpret_cast<bf16*>(a.C2) + wi * a.c_gstride;
+    Run4<bf16>::store(C2 + m * a.ldc + (n - a.c_split), v);
+  } else {
+    Run4<bf16>::store(C + m * a.ldc + n, v);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -630,7 +685,7 @@ template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 hipError_t launch_wgrad(Args a, hipStream_t st) {
   a.tiles_m = (int)((a.M + BM - 1) / BM);
   a.tiles_n = (int)((a.N + BN - 1) / BN);
-  const int64_t grid = (int64_t)a.groups * a.tiles_m * a.tiles_n;
+  const int64_t grid = (int64_t)a.groups * a.tiles_m * a.tiles_n * (EPI == kEpiPartial ? a.ksplit : 1);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)NS * (BM + BN) * BK * 2;
@@ -677,8 +732,26 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
   return hipErrorInvalidValue;
 }
 
+int wgrad_ksplit(int64_t groups, int64_t M, int64_t N, int64_t rows_max) {
+  const int64_t tiles = groups * ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles <= 0 || tiles >= 512) return 1;
+  int64_t s = 512 / tiles;
+  const int64_t by_rows = rows_max / (groups > 0 ? groups : 1) / 1024;  // >= 1024 rows per split
+  if (s > by_rows) s = by_rows;
+  if (s > 8) s = 8;
+  return s < 1 ? 1 : (int)s;
+}
+
 hipError_t run_wgrad_bf16(int epi, const Args& a, hipStream_t st) {
   using namespace gemm;
+  if (a.ksplit > 1) {
+    if (!a.partial || (epi != EPI_STORE && epi != EPI_STORE_SPLITN)) return hipErrorInvalidValue;
+    hipError_t e = launch_wgrad<MOE_GEMM3_CFG_PP, kEpiPartial>(a, st);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = (int64_t)a.groups * a.M * a.N / 4;  // N is a multiple of 8
+    hipLaunchKernelGGL(wgrad_split_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a, epi);
+    return hipGetLastError();
+  }
   if (epi == EPI_STORE) return launch_wgrad<MOE_GEMM3_CFG_PP, EPI_STORE>(a, st);
   if (epi == EPI_STORE_SPLITN) return launch_wgrad<MOE_GEMM3_CFG_PP, EPI_STORE_SPLITN>(a, st);
   return hipErrorInvalidValue;

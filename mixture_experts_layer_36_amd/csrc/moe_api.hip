@@ -50,20 +50,44 @@ int64_t capacity_of(const moe_config* c) {
   return v >= (double)c->T ? c->T : (int64_t)v;
 }
 
+int64_t plan_n_max(const moe_config* c) {
+  const int64_t tk = c->T * c->k, ec = c->E * capacity_of(c);
+  return tk < ec ? tk : ec;
+}
+
 size_t elem_bytes(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 struct WsLayout {
   size_t dispatch, route, route_bwd, ffn_routed, ffn_shared, total;
 };
 
+// Workspace of one moe_expert_ffn_bwd call over `groups` groups of hidden
+// width F and at most rows_max rows: d_act [rows, m F] in the dtype, then
+// (bf16) the fp32 partials of the split weight-gradient launches.
+size_t ffn_d_act_bytes(const moe_config* c, int64_t F, int64_t rows_max) {
+  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  return round_up((size_t)rows_max * m * F * elem_bytes(c), 256);
+}
+size_t ffn_split_bytes(const moe_config* c, int64_t groups, int64_t F, int64_t rows_max) {
+  if (c->dtype != MOE_BF16) return 0;
+  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  const int64_t s3 = moe::gemm3::wgrad_ksplit(groups, F, c->d, rows_max);
+  const int64_t s4 = moe::gemm3::wgrad_ksplit(groups, c->d, m * F, rows_max);
+  const size_t b3 = s3 > 1 ? (size_t)s3 * groups * F * c->d * 4 : 0;
+  const size_t b4 = s4 > 1 ? (size_t)s4 * groups * c->d * m * F * 4 : 0;
+  return round_up(b3 > b4 ? b3 : b4, 256);
+}
+size_t ffn_bwd_ws(const moe_config* c, int64_t groups, int64_t F, int64_t rows_max) {
+  return ffn_d_act_bytes(c, F, rows_max) + ffn_split_bytes(c, groups, F, rows_max);
+}
+
 WsLayout ws_layout(const moe_config* c, int64_t n_max) {
   WsLayout w;
   const int64_t nb = (c->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
   w.dispatch = round_up((size_t)nb * c->E * 4, 256) * 2 + round_up((size_t)c->E * 8, 256);
   w.route_bwd = round_up((size_t)moe::router_wgrad_blocks(c->T) * c->d * c->E * 4, 256);
-  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
-  w.ffn_routed = round_up((size_t)n_max * m * c->ffn * elem_bytes(c), 256);
-  w.ffn_shared = c->n_shared > 0 ? round_up((size_t)c->T * m * c->n_shared * c->ffn_shared * elem_bytes(c), 256) : 0;
+  w.ffn_routed = ffn_bwd_ws(c, c->E, c->ffn, n_max);
+  w.ffn_shared = c->n_shared > 0 ? ffn_bwd_ws(c, 1, c->n_shared * c->ffn_shared, c->T) : 0;
   w.route = c->dtype == MOE_BF16 ? round_up((size_t)c->d * c->E * 2, 256) : 0;
   w.total = w.dispatch;
   if (w.route > w.total) w.total = w.route;
@@ -158,12 +182,22 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
   a2.C = dx; a2.ldc = d;
   e = run_rows<T>(KIND_DGRAD, EPI_STORE, a2, g->rows_max, st);
   if (e != hipSuccess) return e;
+  // Launches with few tiles split their reduction (bf16), with fp32 partials
+  // placed after d_act in ws, as long as the workspace moe_plan sized holds
+  // them (it does for the routed call over all experts and the shared call).
+  const bool split_ok = std::is_same<T, moe::bf16>::value &&
+                        ffn_bwd_ws(c, g->groups, F, g->rows_max) <= ws_layout(c, plan_n_max(c)).total;
+  float* partial = (float*)((char*)ws + ffn_d_act_bytes(c, F, g->rows_max));
   // 3. dW_out = h^T dy
   Args a3;
   fill_placement(c, g, a3);
   a3.A = h; a3.lda = F; a3.M = F;
   a3.B = dy; a3.ldb = d; a3.N = d;
   a3.C = dw_out; a3.ldc = d; a3.c_gstride = F * d;
+  if (split_ok) {
+    a3.ksplit = moe::gemm3::wgrad_ksplit(g->groups, F, d, g->rows_max);
+    a3.partial = partial;
+  }
   e = run_wgrad<T>(EPI_STORE, a3, st);
   if (e != hipSuccess) return e;
   // 4. dW_in (| dW_up) = x^T d_act
@@ -173,6 +207,10 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
   a4.B = ws; a4.ldb = m * F; a4.N = m * F;
   a4.C = dw_in; a4.C2 = swiglu ? dw_up : nullptr; a4.ldc = F; a4.c_gstride = d * F;
   a4.c_split = F;
+  if (split_ok) {
+    a4.ksplit = moe::gemm3::wgrad_ksplit(g->groups, d, m * F, g->rows_max);
+    a4.partial = partial;
+  }
   return run_wgrad<T>(swiglu ? EPI_STORE_SPLITN : EPI_STORE, a4, st);
 }
 

@@ -97,6 +97,14 @@ FUZZ = {
     "T70_E20_f32": W("T70_E20_f32", T=70, d=56, ffn=32, E=20, k=1, capacity_factor=2.0,
                      gating="softmax_topk", act="gelu", dtype="f32", ep_ranks=4, placement="round_robin",
                      seed=26),
+    # weight-gradient launches with few tiles and long reductions split the
+    # reduction into fp32 partials: the shared experts here (4 splits of
+    # 1024 tokens) and the 2 routed experts of the next case (4 splits)
+    "T4096_shared_splitk": W("T4096_shared_splitk", T=4096, d=64, ffn=32, E=8, k=2, capacity_factor=0.0,
+                             gating="softmax_topk", act="swiglu", dtype="bf16", n_shared=2, ffn_shared=32,
+                             seed=27),
+    "T8192_E2_splitk": W("T8192_E2_splitk", T=8192, d=64, ffn=48, E=2, k=1, capacity_factor=0.0,
+                         gating="softmax_topk", act="gelu", dtype="bf16", seed=28),
 }
 
 
