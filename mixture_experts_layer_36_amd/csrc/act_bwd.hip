@@ -7,52 +7,87 @@
 // d_act [rows, 2F] holds dH in its first F columns on entry and [dA | dB] on
 // exit (in place: every element is read and then written by one thread);
 // act [rows, 2F] is the saved [A | B].  Only rows below the kept-row count
-// offsets[groups] (read on the device) are touched.  Each thread moves 8
-// consecutive columns of one row with 16-byte accesses.
+// offsets[groups] (read on the device) are touched.  Each access moves 16
+// bytes (8 bf16 or 4 fp32 columns).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <typename T>
+// A workgroup walks blocks of RB consecutive rows (grid-stride over row
+// blocks), RB chosen on the host so that a block holds at least 256 U chunks
+// when rows are short.  Per round a thread takes U chunks f = tid + 256 k of
+// the block (row f / cpr, chunk f % cpr) and issues all their loads before any
+// arithmetic or store.
+template <typename T, int U>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(T* __restrict__ d_act, const T* __restrict__ act,
                                                          const int64_t* __restrict__ offsets, int groups,
-                                                         int64_t F) {
+                                                         int64_t F, int RB) {
   constexpr int V = Vec16<T>::N;
   const int64_t rows = offsets[groups];
-  const int64_t cpr = F / V;  // chunks per row (F is a multiple of 8)
-  const int64_t total = rows * cpr;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cpr, c = (i - r * cpr) * V;
-    T* dr = d_act + r * 2 * F;
-    const T* ar = act + r * 2 * F;
-    float dh[V], av[V], bv[V], da[V], db[V];
-    unpack16<T>(ld16(dr + c), dh);
-    unpack16<T>(ld16(ar + c), av);
-    unpack16<T>(ld16(ar + F + c), bv);
+  const uint32_t cpr = (uint32_t)(F / V);  // chunks per row (F is a multiple of 8)
+  for (int64_t r0 = (int64_t)blockIdx.x * RB; r0 < rows; r0 += (int64_t)gridDim.x * RB) {
+    T* dr = d_act + r0 * 2 * F;
+    const T* ar = act + r0 * 2 * F;
+    const uint32_t n = (uint32_t)min((int64_t)RB, rows - r0) * cpr;
+    for (uint32_t f0 = threadIdx.x; f0 < n; f0 += 256 * U) {
+      int64_t off[U];
+      u32x4 h[U], a[U], b[U];
 #pragma unroll
-    for (int q = 0; q < V; ++q) {
-      const float s = 1.0f / (1.0f + __expf(-av[q]));
-      da[q] = dh[q] * bv[q] * s * (1.0f + av[q] * (1.0f - s));
-      db[q] = dh[q] * av[q] * s;
+      for (int k = 0; k < U; ++k) {
+        // chunks past the block load its first chunk and store nothing
+        const uint32_t f = f0 + 256 * k < n ? f0 + 256 * k : 0;
+        const uint32_t row = f / cpr, col = f - row * cpr;
+        off[k] = (int64_t)row * 2 * F + col * V;
+        h[k] = ld16(dr + off[k]);
+        a[k] = ld16(ar + off[k]);
+        b[k] = ld16(ar + off[k] + F);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        float dh[V], av[V], bv[V], da[V], db[V];
+        unpack16<T>(h[k], dh);
+        unpack16<T>(a[k], av);
+        unpack16<T>(b[k], bv);
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          const float s = 1.0f / (1.0f + __expf(-av[q]));
+          da[q] = dh[q] * bv[q] * s * (1.0f + av[q] * (1.0f - s));
+          db[q] = dh[q] * av[q] * s;
+        }
+        if (f0 + 256 * k < n) {
+          st16(dr + off[k], pack16<T>(da));
+          st16(dr + off[k] + F, pack16<T>(db));
+        }
+      }
     }
-    st16(dr + c, pack16<T>(da));
-    st16(dr + F + c, pack16<T>(db));
   }
+}
+
+template <typename T>
+static void launch_swiglu_bwd_t(T* d_act, const T* act, const int64_t* offsets, int groups, int64_t rows_max,
+                                int64_t F, hipStream_t st) {
+  const int64_t cpr = F / Vec16<T>::N;
+  const int U = cpr > 512 ? 4 : 2;
+  const int64_t RB = cpr >= 256 * U ? 1 : (256 * U) / cpr;  // rows per block
+  int64_t blocks = (rows_max + RB - 1) / RB;
+  if (blocks > 8192) blocks = 8192;  // row blocks beyond: grid-stride
+  if (U == 4)
+    hipLaunchKernelGGL((swiglu_bwd_kernel<T, 4>), dim3((unsigned)blocks), dim3(256), 0, st, d_act, act, offsets,
+                       groups, F, (int)RB);
+  else
+    hipLaunchKernelGGL((swiglu_bwd_kernel<T, 2>), dim3((unsigned)blocks), dim3(256), 0, st, d_act, act, offsets,
+                       groups, F, (int)RB);
 }
 
 hipError_t launch_swiglu_bwd(void* d_act, const void* act, const int64_t* offsets, int groups, int64_t rows_max,
                              int64_t F, bool bf16_dtype, hipStream_t st) {
-  const int64_t chunks = rows_max * (F / (bf16_dtype ? 8 : 4));
-  if (chunks <= 0) return hipSuccess;
-  int64_t blocks = (chunks + 255) / 256;
-  if (blocks > 65536) blocks = 65536;  // grid-stride beyond
+  if (rows_max <= 0 || F <= 0) return hipSuccess;
+  if (F / (bf16_dtype ? 8 : 4) > (1 << 20)) return hipErrorInvalidValue;  // chunk indices stay 32-bit
   if (bf16_dtype)
-    hipLaunchKernelGGL((swiglu_bwd_kernel<bf16>), dim3((unsigned)blocks), dim3(256), 0, st, (bf16*)d_act,
-                       (const bf16*)act, offsets, groups, F);
+    launch_swiglu_bwd_t<bf16>((bf16*)d_act, (const bf16*)act, offsets, groups, rows_max, F, st);
   else
-    hipLaunchKernelGGL((swiglu_bwd_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st, (float*)d_act,
-                       (const float*)act, offsets, groups, F);
+    launch_swiglu_bwd_t<float>((float*)d_act, (const float*)act, offsets, groups, rows_max, F, st);
   return hipGetLastError();
 }
 

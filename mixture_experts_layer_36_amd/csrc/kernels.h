@@ -8,7 +8,7 @@ namespace moe {
 constexpr int kDispatchBlock = 256;  // tokens per block of the stable-rank kernels
 
 struct RouteArgs {
-  const void* x; const void* w; uint32_t* wpack;  // wpack: workspace, bf16 weight pairs
+  const void* x; const void* w; uint32_t* wpack;  // wpack: workspace, bf16 weights in MFMA operand order
   const float* bias;
   float* logits; int32_t* topk_idx; float* topk_w;
   int64_t T; int d; int E; int k; int gating;
@@ -44,6 +44,8 @@ struct DispatchBwdArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st);
+// bytes of ws the bf16 route uses for its re-packed copy of w_router
+size_t route_ws_bytes(int64_t d, int64_t E);
 hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t st);

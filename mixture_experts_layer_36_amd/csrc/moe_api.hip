@@ -88,7 +88,7 @@ WsLayout ws_layout(const moe_config* c, int64_t n_max) {
   w.route_bwd = round_up((size_t)moe::router_wgrad_blocks(c->T) * c->d * c->E * 4, 256);
   w.ffn_routed = ffn_bwd_ws(c, c->E, c->ffn, n_max);
   w.ffn_shared = c->n_shared > 0 ? ffn_bwd_ws(c, 1, c->n_shared * c->ffn_shared, c->T) : 0;
-  w.route = c->dtype == MOE_BF16 ? round_up((size_t)c->d * c->E * 2, 256) : 0;
+  w.route = c->dtype == MOE_BF16 ? round_up(moe::route_ws_bytes(c->d, c->E), 256) : 0;
   w.total = w.dispatch;
   if (w.route > w.total) w.total = w.route;
   if (w.route_bwd > w.total) w.total = w.route_bwd;
