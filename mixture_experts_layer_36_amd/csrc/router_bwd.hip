@@ -157,6 +157,111 @@ __global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_partial_kernel(co
   }
 }
 
+// partial[b][i][e] on the fp32 matrix cores: v_mfma_f32_16x16x4_f32 takes
+// A[m][kk] from lane kk * 16 + m and B[kk][n] from lane kk * 16 + n, so 4
+// tokens x 16 columns of x and 4 tokens x 16 experts of dlogits enter as one
+// value per lane, with no transposition.  A lane loads 16 bytes of x (V
+// consecutive columns c0 + V m + j of token t = 4-group base + lane / 16) and
+// feeds value j to the MFMA of column block j: block j's row m is column
+// c0 + V m + j, so one workgroup covers CW = 16 V columns.  The products are
+// exact in fp32 and summed in fp32 in a fixed order, as before; the 4 waves
+// take consecutive quarters of the block's tokens (4 token groups per round,
+// loads first) and their accumulators are summed in a fixed tree through LDS.
+template <typename T, int EP>
+__global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_mfma_kernel(const T* __restrict__ x,
+                                                                           const float* __restrict__ dl,
+                                                                           float* __restrict__ partial, int64_t Tn,
+                                                                           int d, int E, int tw) {
+  constexpr int V = Vec16<T>::N, NB = EP / 16, CW = 16 * V, U = 4;
+  constexpr int NACC = V * NB;  // f32x4 accumulators per lane
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kk = lane >> 4, m = lane & 15;
+  const int c0 = blockIdx.x * CW + V * m;  // this lane's first x column
+  const bool col_ok = c0 < d;              // d is a multiple of 8: all V columns in or out
+  const int64_t tbeg = ((int64_t)blockIdx.y * kRwgWaves + wave) * tw;
+  const int64_t tend = tbeg + tw < Tn ? tbeg + tw : Tn;
+  f32x4 acc[V][NB];
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // token group at t4: lane's token t4 + kk; unconditional loads from valid
+  // addresses, zeros by select past the range, the last column or E
+  auto load = [&](int64_t t4, u32x4& xv, float (&dv)[NB]) {
+    const int64_t t = t4 + kk;
+    const bool tok = t < tend;
+    const int64_t tc = tok ? t : tbeg;
+    const u32x4 v = ld16(x + tc * d + (col_ok ? c0 : 0));
+    xv = (tok && col_ok) ? v : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = 16 * nb + m;
+      const float w = dl[tc * E + (e < E ? e : E - 1)];
+      dv[nb] = (tok && e < E) ? w : 0.0f;
+    }
+  };
+  for (int64_t t = tbeg; t < tend; t += 4 * U) {
+    u32x4 xv[U];
+    float dv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(t + 4 * u, xv[u], dv[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float xf[V];
+      unpack16<T>(xv[u], xf);
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[j], dv[u][nb], acc[j][nb], 0, 0, 0);
+    }
+  }
+  // fixed-order tree sum of the 4 waves' accumulators: (w2 + w3) into w0, w1; then w1 into w0
+  float* red = reinterpret_cast<float*>(lds);  // [2][NACC * 4][64]
+  if (wave >= 2) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(((wave - 2) * NACC + j * NB + nb) * 4 + q) * 64 + lane] = acc[j][nb][q];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j][nb][q] += red[((wave * NACC + j * NB + nb) * 4 + q) * 64 + lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[((j * NB + nb) * 4 + q) * 64 + lane] = acc[j][nb][q];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // accumulator (j, nb)[q] of lane l: column blockIdx.x CW + V (4 (l / 16) + q) + j, expert 16 nb + l % 16
+  float* pb = partial + (int64_t)blockIdx.y * d * E;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = acc[j][nb][q] + red[((j * NB + nb) * 4 + q) * 64 + lane];
+        const int col = blockIdx.x * CW + V * (4 * kk + q) + j, e = 16 * nb + m;
+        if (col < d && e < E) pb[(int64_t)col * E + e] = v;
+      }
+}
+
 // dw[i] = sum over b in order of partial[b][i].  A thread owns 4 consecutive
 // outputs and loads all its partials (nb <= 64, 16-byte loads) before the
 // in-order sums, so the loads overlap instead of following one another.
@@ -207,12 +312,40 @@ static hipError_t launch_rwg(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T, int EP>
+static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
+  constexpr int V = Vec16<T>::N, CW = 16 * V;
+  constexpr size_t lds = (size_t)2 * V * (EP / 16) * 4 * 64 * 4;
+  const int nb = router_wgrad_blocks(a.T);
+  const int tw = (int)((a.T + (int64_t)nb * kRwgWaves - 1) / ((int64_t)nb * kRwgWaves));  // tokens per wave
+  const dim3 grid((unsigned)((a.d + CW - 1) / CW), nb);
+  auto kern = router_wgrad_mfma_kernel<T, EP>;
+  if constexpr (lds > 65536) {
+    static const hipError_t prep = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (prep != hipSuccess) return prep;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kRwgWaves), lds, st, (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d,
+                     a.E, tw);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t dE = a.d * a.E;
+  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
+                     a.partial, nb, dE, (T*)a.dw_router);
+  return hipGetLastError();
+}
+
+// bf16 x with up to 16 experts: the vector kernel, bound by reading x (the
+// fp32 MFMA pads E to 16 and measured slower on the Mixtral shape, 0.059
+// against 0.049 ms for the whole router backward).  More experts, or fp32 x:
+// the fp32 MFMA kernel (DeepSeek-V2-Lite shape 0.187 -> 0.137 ms).
 template <typename T>
 static hipError_t launch_rwg_dt(const RouteBwdArgs& a, hipStream_t st) {
-  if (a.E <= 8) return launch_rwg<T, 8>(a, st);
-  if (a.E <= 16) return launch_rwg<T, 16>(a, st);
-  if (a.E <= 32) return launch_rwg<T, 32>(a, st);
-  return launch_rwg<T, 64>(a, st);
+  if (sizeof(T) == 2 && a.E <= 8) return launch_rwg<T, 8>(a, st);
+  if (sizeof(T) == 2 && a.E <= 16) return launch_rwg<T, 16>(a, st);
+  if (a.E <= 16) return launch_rwg_mfma<T, 16>(a, st);
+  if (a.E <= 32) return launch_rwg_mfma<T, 32>(a, st);
+  return launch_rwg_mfma<T, 64>(a, st);
 }
 
 int router_wgrad_blocks(int64_t T) {
