@@ -417,6 +417,158 @@ __device__ __forceinline__ void k_loop_pingpong(char* smem, int nk, int group, c
   if (group == 0) barrier();
 }
 
+// ---------------------------------------------------------------------------
+// Staged epilogues (ping-pong kernels, 256 x 256 tiles of 8 waves in 2 x 4).
+// Stored straight from the accumulators, a store instruction writes 8 bytes
+// into each of 32 rows: partial L2 lines, which the output of every tile of a
+// round competes for at once, and which measured as the whole per-tile cost
+// beyond the K loop (up to a quarter of a short-K launch).  Instead, once the
+// K loop is done and its ring idle, each 32-row pass of the accumulators
+// (rows wm0 + 32 i + 0..31 of every wave) is written into an LDS table of 64
+// staged rows (wave row band wm: staged rows 32 wm + 0..31) and SC columns,
+// and the workgroup then stores the table in 16-byte chunks, consecutive
+// threads on consecutive chunks of one row, so every row goes out as whole
+// lines.  16-byte chunk c of staged row r sits at chunk c ^ (r & 15): the
+// 8-byte writes (32 rows, one column) are at most 2-way bank conflicted and
+// the 16-byte reads (16 consecutive chunks of a row) are conflict-free.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <typename T, int SC>
+struct StagedTile {
+  static constexpr int ROWB = SC * (int)sizeof(T), CH = ROWB / 16, ROWS = 64;
+  static_assert(ROWB % 256 == 0, "rows of whole 256-byte bank windows");
+  lds_char* base;
+  // 4 consecutive values at element column col (a multiple of 4) of staged row r
+  __device__ __forceinline__ void put4(int r, int col, const float (&v)[4]) const {
+    const int byte = col * (int)sizeof(T);
+    lds_char* p = base + r * ROWB + (((byte >> 4) ^ (r & 15)) << 4) + (byte & 15);
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(p) =
+          u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    else
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+  __device__ __forceinline__ u32x4 get(int r, int c) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + r * ROWB + ((c ^ (r & 15)) << 4));
+  }
+  // every thread of the workgroup: chunk q = tid + NT k of the table, handed
+  // to dst(staged row, element column of the chunk, data)
+  template <int NT, typename Dst>
+  __device__ __forceinline__ void store_all(const Dst& dst) const {
+#pragma unroll
+    for (int q = (int)threadIdx.x; q < ROWS * CH; q += NT) {
+      const int r = q / CH, c = q - r * CH;
+      dst(r, c * (16 / (int)sizeof(T)), get(r, c));
+    }
+  }
+};
+
+// Row-split kernels: EPI_STORE (C), EPI_GELU_FWD (C = Z | C2 = GELU(Z)) and the
+// SwiGLU gate|up pair (C = A | B at column f and c_split + f, C2 = silu(A) B).
+template <int FM, int FN, bool PAIR, int EPI>
+__device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                                     int wave, int lane, int64_t row_begin, int64_t row_end,
+                                                     int64_t n0, int64_t N, char* smem) {
+  static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
+  constexpr bool GELU = EPI == gemm::EPI_GELU_FWD;
+  constexpr int SC = PAIR ? 384 : (GELU ? 512 : 256);  // PAIR: A | B | H; GELU: Z | GELU(Z)
+  const StagedTile<bf16, SC> st{(lds_char*)smem};
+  bf16* C = reinterpret_cast<bf16*>(a.C);
+  bf16* C2 = reinterpret_cast<bf16*>(a.C2);
+  const int wm = wave / 4;
+  const int sr = 32 * wm + (lane & 31);  // this lane's staged row
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    __syncthreads();  // the table's previous pass has been stored (and the K ring is idle)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int tc = tacc_col(g, lane);
+      if constexpr (PAIR) {
+        float av[4], bv[4], hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          av[q] = acc[i][0][4 * g + q];
+          bv[q] = acc[i][1][4 * g + q];
+          hv[q] = av[q] * sigmoid_f(av[q]) * bv[q];
+        }
+        st.put4(sr, bcol[0] + tc, av);
+        st.put4(sr, bcol[1] + tc, bv);
+        st.put4(sr, 256 + bcol[0] + tc, hv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+          st.put4(sr, bcol[j] + tc, v);
+          if constexpr (GELU) {
+            float h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
+            st.put4(sr, 256 + bcol[j] + tc, h);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    st.template store_all<512>([&](int r, int col, const u32x4& v) {
+      const int64_t rr = row_begin + (r >> 5) * 128 + 32 * i + (r & 31);
+      if (rr >= row_end) return;
+      if constexpr (PAIR) {
+        const int part = col >> 7, c = col & 127;  // 0: A, 1: B, 2: H
+        if (n0 + c >= N) return;
+        if (part == 0) st16(C + rr * a.ldc + n0 + c, v);
+        else if (part == 1) st16(C + rr * a.ldc + a.c_split + n0 + c, v);
+        else st16(C2 + rr * a.ldc2 + n0 + c, v);
+      } else {
+        const int c = col & 255;
+        if (n0 + c >= N) return;
+        if (GELU && col >= 256) st16(C2 + rr * a.ldc2 + n0 + c, v);
+        else st16(C + rr * a.ldc + n0 + c, v);
+      }
+    });
+  }
+}
+
+// WGRAD kernels: weight set wi, rows m0 + ..., columns n0 + ... (EPI_STORE_SPLITN
+// sends columns >= c_split to C2); T = float for the split partials.
+template <typename T, int FM, int FN, int EPI>
+__device__ __forceinline__ void wgrad_epilogue_staged(const Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                                      int wave, int lane, int wi, int64_t m0, int64_t n0, int64_t M,
+                                                      int64_t N, char* smem) {
+  static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
+  const StagedTile<T, 256> st{(lds_char*)smem};
+  T* C = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride;
+  T* C2 = a.C2 ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride : nullptr;
+  const int wm = wave / 4;
+  const int sr = 32 * wm + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+        st.put4(sr, bcol[j] + tacc_col(g, lane), v);
+      }
+    __syncthreads();
+    st.template store_all<512>([&](int r, int col, const u32x4& v) {
+      const int64_t m = m0 + (r >> 5) * 128 + 32 * i + (r & 31);
+      const int64_t n = n0 + col;
+      if (m >= M || n >= N) return;
+      // c_split is a multiple of 8: a chunk never straddles it
+      if (EPI == gemm::EPI_STORE_SPLITN && n >= a.c_split)
+        st16(C2 + m * a.ldc + (n - a.c_split), v);
+      else
+        st16(C + m * a.ldc + n, v);
+    });
+  }
+}
+
 constexpr int kPingPong = -1;  // NP value selecting the ping-pong loop
 // WGRAD epilogue selector (internal) of a launch split over the reduction:
 // each split writes an fp32 partial [split][weight set][M][N], summed after
@@ -525,7 +677,11 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
     k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
   }
 
-  rows_epilogue_t<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
+  if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
+                (EPI == gemm::EPI_STORE || EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD))
+    rows_epilogue_staged<FM, FN, PAIR, EPI>(a, acc, bcol, wave, lane, row_begin, row_end, n0, N, smem);
+  else
+    rows_epilogue_t<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,9 +788,15 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
     ap.C2 = nullptr;
     ap.ldc = N;
     ap.c_gstride = M * N;
-    wgrad_epilogue_t<float, FM, FN, gemm::EPI_STORE>(ap, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+    if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4)
+      wgrad_epilogue_staged<float, FM, FN, gemm::EPI_STORE>(ap, acc, bcol, wave, lane, wi, m0, n0, M, N, smem);
+    else
+      wgrad_epilogue_t<float, FM, FN, gemm::EPI_STORE>(ap, acc, bcol, wm0, lane, wi, m0, n0, M, N);
   } else {
-    wgrad_epilogue_t<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
+    if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4)
+      wgrad_epilogue_staged<bf16, FM, FN, EPI>(a, acc, bcol, wave, lane, wi, m0, n0, M, N, smem);
+    else
+      wgrad_epilogue_t<bf16, FM, FN, EPI>(a, acc, bcol, wm0, lane, wi, m0, n0, M, N);
   }
 }
 
