@@ -531,6 +531,88 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
   }
 }
 
+// Activation backward of the row-split DGRAD kernels, staged the same way:
+// dZ = acc * GELU'(Z) (X1 = Z), or for SwiGLU with X1 = [A | B]:
+// dA = acc * B * s * (1 + A (1 - s)), dB = acc * silu(A) (s = sigmoid(A)),
+// stored at columns n and c_split + n of C.  The accumulators are staged in
+// fp32; a thread then takes 8 consecutive columns of a staged row, with all
+// its 16-byte loads of the saved activations for the pass issued before any
+// arithmetic, and stores 16 bytes per output.
+template <int FM, int FN, int EPI>
+__device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
+                                                         int wave, int lane, int64_t row_begin, int64_t row_end,
+                                                         int64_t n0, int64_t N, char* smem) {
+  static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
+  constexpr bool SW = EPI == gemm::EPI_SWIGLU_BWD;
+  constexpr int PER = 64 * 32 / 512;  // 8-column groups per thread per pass
+  const StagedTile<float, 256> st{(lds_char*)smem};
+  bf16* C = reinterpret_cast<bf16*>(a.C);
+  const bf16* X1 = reinterpret_cast<const bf16*>(a.X1);
+  const int sr = 32 * (wave / 4) + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+        st.put4(sr, bcol[j] + tacc_col(g, lane), v);
+      }
+    __syncthreads();
+    // group u of this thread: staged row r = q / 32, columns 8 (q % 32) .. +7
+    int64_t rr[PER], nn[PER];
+    bool ok[PER];
+    u32x4 x0[PER], x1[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = (int)threadIdx.x + 512 * u, r = q >> 5, c8 = (q & 31) * 8;
+      rr[u] = row_begin + (r >> 5) * 128 + 32 * i + (r & 31);
+      nn[u] = n0 + c8;
+      ok[u] = rr[u] < row_end && nn[u] < N;
+      // unconditional loads from a valid place (the tile's first row and column) when out of range
+      const bf16* xp = X1 + (ok[u] ? rr[u] * a.ldx + nn[u] : row_begin * a.ldx + n0);
+      x0[u] = ld16(xp);
+      if constexpr (SW) x1[u] = ld16(xp + a.c_split);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = (int)threadIdx.x + 512 * u, r = q >> 5, c = (q & 31) * 2;  // two fp32 chunks
+      float g8[8], z[8];
+      {
+        const u32x4 lo = st.get(r, c), hi = st.get(r, c + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g8[e] = __uint_as_float(lo[e]);
+          g8[4 + e] = __uint_as_float(hi[e]);
+        }
+      }
+      unpack16<bf16>(x0[u], z);
+      if constexpr (SW) {
+        float bv[8], da[8], db[8];
+        unpack16<bf16>(x1[u], bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = sigmoid_f(z[e]);
+          da[e] = g8[e] * bv[e] * sg * (1.0f + z[e] * (1.0f - sg));
+          db[e] = g8[e] * z[e] * sg;
+        }
+        if (ok[u]) {
+          st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(da));
+          st16(C + rr[u] * a.ldc + a.c_split + nn[u], pack16<bf16>(db));
+        }
+      } else {
+        float dz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dz[e] = g8[e] * gelu_grad_f(z[e]);
+        if (ok[u]) st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(dz));
+      }
+    }
+  }
+}
+
 // WGRAD kernels: weight set wi, rows m0 + ..., columns n0 + ... (EPI_STORE_SPLITN
 // sends columns >= c_split to C2); T = float for the split partials.
 template <typename T, int FM, int FN, int EPI>
@@ -680,6 +762,9 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
   if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
                 (EPI == gemm::EPI_STORE || EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD))
     rows_epilogue_staged<FM, FN, PAIR, EPI>(a, acc, bcol, wave, lane, row_begin, row_end, n0, N, smem);
+  else if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
+                     (EPI == gemm::EPI_GELU_BWD || EPI == gemm::EPI_SWIGLU_BWD))
+    rows_epilogue_staged_bwd<FM, FN, EPI>(a, acc, bcol, wave, lane, row_begin, row_end, n0, N, smem);
   else
     rows_epilogue_t<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
@@ -858,19 +943,12 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile configurations (BM, BN, WM, WN, BK, NS, NP), from measurements of the
-// Mixtral-sized expert GEMMs (d 4096, F 14336):
-//  * CFG_PP: 256x256 tile, 8 waves in two ping-pong groups, K-step 32,
-//    4-stage ring: forward, plain dgrad and wgrad launches.
-//  * CFG_ACT_BWD: 256x128 tile, 4 MFMA waves fed by 4 load-only waves, K-step
-//    64, 3-stage ring: the SwiGLU dgrad launch, whose epilogue reads the saved
-//    gate and up activations (34% against 32% for CFG_PP on the Mixtral
-//    shape; the GELU' launches of the smaller workloads measured faster with
-//    CFG_PP).
-// (All 8 waves in lockstep and 4-wave 256x256 tiles measured slower for
-// every kind.)
+// Tile configuration (BM, BN, WM, WN, BK, NS, NP), from measurements of the
+// Mixtral-sized expert GEMMs (d 4096, F 14336): a 256 x 256 tile, 8 waves in
+// two ping-pong groups, K-step 32, 4-stage ring, for every kind.  (All 8
+// waves in lockstep, 4 MFMA waves fed by 4 load-only waves on 256 x 128
+// tiles, and 4-wave 256 x 256 tiles measured slower.)
 #define MOE_GEMM3_CFG_PP 256, 256, 2, 4, 32, 4, -1
-#define MOE_GEMM3_CFG_ACT_BWD 256, 128, 2, 2, 64, 3, 4
 
 // Whether the direct-load kernels take this launch: the K split of the SwiGLU
 // dgrad (gate | up weights) must fall on a stage boundary.
@@ -888,7 +966,7 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
     switch (epi) {
       case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_STORE>(a, rows_max, st);
       case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_GELU_BWD>(a, rows_max, st);
-      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_ACT_BWD, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_DGRAD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   }
   return hipErrorInvalidValue;

@@ -51,11 +51,6 @@ hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st)
 hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st);
-// SwiGLU backward in place on d_act [rows, 2F] (dH in the first F columns on
-// entry, [dA | dB] on exit) from the saved act [rows, 2F] = [A | B]; rows =
-// offsets[groups], read on the device, at most rows_max.
-hipError_t launch_swiglu_bwd(void* d_act, const void* act, const int64_t* offsets, int groups, int64_t rows_max,
-                             int64_t F, bool bf16_dtype, hipStream_t st);
 
 int router_wgrad_blocks(int64_t T);
 

@@ -152,12 +152,7 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
   const bool swiglu = c->act == MOE_ACT_SWIGLU;
   const int64_t m = swiglu ? 2 : 1;
   // 1. dgrad through W_out and the activation backward: d_act in ws.  GELU'
-  //    is fused into the GEMM's epilogue.  For bf16 SwiGLU the GEMM stores dH
-  //    into the first F columns of d_act and a bandwidth kernel then turns it
-  //    into [dA | dB] in place: the fused epilogue's reads of the saved
-  //    [A | B] idle the matrix cores, the separate pass streams them at HBM
-  //    rate.
-  const bool split_swiglu = swiglu && std::is_same<T, moe::bf16>::value;
+  //    and SwiGLU' are fused into the GEMM's epilogue.
   Args a1;
   fill_placement(c, g, a1);
   a1.A = dy; a1.lda = d;
@@ -165,13 +160,9 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
   a1.N = F; a1.K = d;
   a1.X1 = act_saved; a1.ldx = m * F;
   a1.C = ws; a1.ldc = m * F; a1.c_split = F;
-  const int epi1 = split_swiglu ? EPI_STORE : swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
+  const int epi1 = swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD;
   hipError_t e = run_rows<T>(KIND_DGRAD, epi1, a1, g->rows_max, st);
   if (e != hipSuccess) return e;
-  if (split_swiglu) {
-    e = moe::launch_swiglu_bwd(ws, act_saved, g->offsets, (int)g->groups, g->rows_max, F, true, st);
-    if (e != hipSuccess) return e;
-  }
   // 2. dgrad through W_in (and W_up): dx = d_act . [W_in | W_up]^T
   Args a2;
   fill_placement(c, g, a2);
