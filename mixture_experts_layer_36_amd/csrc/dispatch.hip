@@ -10,8 +10,9 @@
 // Stable positions without order-dependent atomics, in four launches:
 //   1. block_hist: per block of 256 tokens, count the tokens choosing each
 //      expert (integer LDS atomics: the count does not depend on order);
-//   2. scan: one workgroup turns the block counts into per-(block, expert)
-//      bases, raw / kept counts, slot offsets and send segments;
+//   2. scan: one workgroup (wave prefix sums) turns the block counts into
+//      per-(block, expert) bases, raw / kept counts, slot offsets and send
+//      segments;
 //   3. rows: per block, each token's rank among the block's earlier tokens
 //      (64-bit wave ballots + popcount, then a prefix over the 4 waves) gives
 //      pos, the kept flag, the row, row_of and assign_of_row;
@@ -44,55 +45,69 @@ __device__ __forceinline__ int slot_expert(int s, int E, int R, int placement) {
   return placement == 0 ? s : (s % L) * R + s / L;
 }
 
-__global__ __launch_bounds__(64) void scan_kernel(const int32_t* __restrict__ block_counts, int nb, int E, int64_t C,
-                                                  int R, int placement, int32_t* __restrict__ block_base,
-                                                  int32_t* __restrict__ raw_counts, int32_t* __restrict__ kept_counts,
-                                                  int64_t* __restrict__ slot_offsets, int32_t* __restrict__ send_counts,
-                                                  int64_t* __restrict__ send_offsets,
-                                                  int64_t* __restrict__ expert_start) {
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename V>
+__device__ __forceinline__ V wave_incl_scan(V v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const V u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// One workgroup of 16 waves.  Wave w scans the block-count columns of experts
+// w, w + 16, ...: 64 blocks per round, one per lane, by a wave prefix sum plus
+// the carry of the earlier rounds (block_base = exclusive prefix down the
+// column).  Then wave 0 takes one slot per lane for the prefix over the kept
+// counts in slot order, and the send segments.
+constexpr int kScanWaves = 16;
+
+__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
+    const int32_t* __restrict__ block_counts, int nb, int E, int64_t C, int R, int placement,
+    int32_t* __restrict__ block_base, int32_t* __restrict__ raw_counts, int32_t* __restrict__ kept_counts,
+    int64_t* __restrict__ slot_offsets, int32_t* __restrict__ send_counts, int64_t* __restrict__ send_offsets,
+    int64_t* __restrict__ expert_start) {
   __shared__ int64_t kept_s[64];
-  const int e = threadIdx.x;
-  if (e < E) {
-    // running sum down the expert's column of block counts, 16 blocks per
-    // round with their loads issued first
-    int64_t run = 0;
-    for (int b0 = 0; b0 < nb; b0 += 16) {
-      int c[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        // clamped, unconditional load and a select: no branch per load
-        const int b = b0 + u < nb ? b0 + u : nb - 1;
-        const int v = block_counts[(int64_t)b * E + e];
-        c[u] = b0 + u < nb ? v : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (b0 + u >= nb) break;
-        block_base[(int64_t)(b0 + u) * E + e] = (int32_t)run;
-        run += c[u];
-      }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = wave; e < E; e += kScanWaves) {
+    int carry = 0;  // counts are per-token assignments: T * k < 2^31
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      const int v = b < nb ? block_counts[(int64_t)b * E + e] : 0;
+      const int incl = wave_incl_scan(v, lane);
+      if (b < nb) block_base[(int64_t)b * E + e] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
     }
-    raw_counts[e] = (int32_t)run;
-    const int64_t kept = run < C ? run : C;
-    kept_counts[e] = (int32_t)kept;
-    kept_s[e] = kept;
+    if (lane == 0) {
+      raw_counts[e] = carry;
+      const int64_t kept = carry < C ? carry : C;
+      kept_counts[e] = (int32_t)kept;
+      kept_s[e] = kept;
+    }
   }
   __syncthreads();
-  if (e == 0) {
-    int64_t off = 0;
-    for (int s = 0; s < E; ++s) {
-      const int ex = slot_expert(s, E, R, placement);
-      slot_offsets[s] = off;
-      expert_start[ex] = off;
-      off += kept_s[ex];
-    }
-    slot_offsets[E] = off;
-    const int L = E / R;
-    for (int q = 0; q < R; ++q) {
-      send_offsets[q] = slot_offsets[q * L];
-      send_counts[q] = (int32_t)(slot_offsets[(q + 1) * L] - slot_offsets[q * L]);
-    }
-    send_offsets[R] = off;
+  if (wave != 0) return;
+  const int ex = lane < E ? slot_expert(lane, E, R, placement) : 0;
+  const int64_t v = lane < E ? kept_s[ex] : 0;
+  const int64_t incl = wave_incl_scan(v, lane), excl = incl - v;
+  const int64_t total = __shfl(incl, 63, 64);
+  if (lane < E) {
+    slot_offsets[lane] = excl;
+    expert_start[ex] = excl;
+  }
+  // send segment q = lane < R: slots [q L, (q + 1) L)
+  const int L = E / R;
+  const int s0 = lane < R ? lane * L : 0, s1 = lane < R ? (lane + 1) * L : 0;
+  const int64_t o0 = __shfl(excl, s0 & 63, 64);
+  const int64_t o1 = s1 < E ? __shfl(excl, s1 & 63, 64) : total;
+  if (lane < R) {
+    send_offsets[lane] = o0;
+    send_counts[lane] = (int32_t)(o1 - o0);
+  }
+  if (lane == 0) {
+    slot_offsets[E] = total;
+    send_offsets[R] = total;
   }
 }
 
@@ -216,7 +231,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t s
                      a.block_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, st, a.block_counts, nb, a.E, a.C, a.R, a.placement,
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64 * kScanWaves), 0, st, a.block_counts, nb, a.E, a.C, a.R,
+                     a.placement,
                      a.block_base, a.raw_counts, a.expert_counts, a.expert_offsets, a.send_counts, a.send_offsets,
                      a.expert_start);
   err = hipGetLastError();
