@@ -256,9 +256,8 @@ __global__ __launch_bounds__(256) void pack_router_frags_kernel(const uint16_t* 
   wf[i] = u32x4{v[0], v[1], v[2], v[3]};
 }
 
-// A workgroup owns 16 TG tokens; its 8 waves take contiguous ranges of the
-// 32-K blocks, each keeping the x and W blocks of the next P K blocks in
-// flight.  The waves' accumulators are summed in a
+// A workgroup owns 16 TG tokens; its 8 waves take every 8th 32-K block, each
+// keeping the x and W blocks of the next P K blocks in flight.  The waves' accumulators are summed in a
 // fixed binary tree through LDS (deterministic logits), wave 0 spreads them
 // to a [16 TG][EP] table and lane t finishes token t.
 template <int EP, int TG, int PER, int P>
@@ -272,8 +271,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t0 = (int64_t)blockIdx.x * TOK;
   const int nkb = (d + 31) / 32;
-  const int per = (nkb + kMfmaWaves - 1) / kMfmaWaves;
-  const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+  // wave w takes the 32-K blocks w, w + 8, w + 16, ...: at any time the 8
+  // waves read neighbouring 64-byte pieces of the same rows
+  const int nw = wave < nkb ? (nkb - wave + kMfmaWaves - 1) / kMfmaWaves : 0;  // blocks of this wave
 
   // this lane's x rows: token t0 + 16 tg + lane % 16 (row t0 when past T),
   // K offset 8 (lane / 16) within each 32-K block
@@ -288,9 +288,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_mfma_kernel(
   }
   // K block kb of this wave's range, clamped: blocks past the range load the
   // last one again with a zero x operand (no branch around the loads)
-  auto load = [&](int kb, u32x4 (&a)[TG], u32x4 (&b)[NB]) {
-    const bool kin = kb < kb1;
-    const int kc = kin ? kb : kb1 - 1;
+  auto load = [&](int i, u32x4 (&a)[TG], u32x4 (&b)[NB]) {
+    const bool kin = i < nw;
+    const int kc = wave + kMfmaWaves * (kin ? i : nw - 1);
     const int kx = 32 * kc + 8 * g;
     const bool kok = kin && kx < d;  // d is a multiple of 8: a piece is all in or all out
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_mfma_kernel(
   // loads P blocks ahead of their MFMAs, no loop-carried load registers (a
   // rotating register buffer across loop iterations makes the compiler copy
   // it and wait for every load)
-  for (int c0 = kb0; c0 < kb1; c0 += PER) {
+  for (int c0 = 0; c0 < nw; c0 += PER) {
     u32x4 a[PER][TG], b[PER][NB];
 #pragma unroll
     for (int i = 0; i < P && i < PER; ++i) load(c0 + i, a[i], b[i]);
@@ -386,7 +386,7 @@ static hipError_t launch_route_mfma(const RouteArgs& a, hipStream_t st) {
   constexpr size_t tab = (size_t)16 * TG * EP * 4;
   constexpr size_t lds = red > tab ? red : tab;
   constexpr int P = EP == 16 ? 4 : 2;  // K blocks in flight per wave
-  const int per = ((a.d + 31) / 32 + kMfmaWaves - 1) / kMfmaWaves;  // K blocks per wave
+  const int per = ((a.d + 31) / 32 + kMfmaWaves - 1) / kMfmaWaves;  // most K blocks of a wave
 #define MOE_ROUTE_MFMA(PER)                                                                                     \
   hipLaunchKernelGGL((route_mfma_kernel<EP, TG, PER, P>), dim3((unsigned)blocks), dim3(kMfmaWaves * 64), lds, st, \
                      (const bf16*)a.x, (const u32x4*)a.wpack, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d,   \
