@@ -20,10 +20,11 @@
 //    K-contiguous operands (the activation rows of FWD / DGRAD, the weights
 //    of DGRAD) are stored [rows][BK] and read with ds_read_b128.
 //
-// Synchronisation per stage: wait until this wave's loads of the stage have
-// landed (vmcnt), barrier (all waves' loads landed and all waves finished the
-// previous stage), issue the loads of stage kt + NS - 1 into the slot the
-// previous stage used, multiply the current stage.
+// Schedule: the 8 waves form two ping-pong groups (k_loop_pingpong), one wave
+// of each on every SIMD; per stage a wave runs a memory phase (its share of
+// the loads NS - 1 stages ahead, then all fragment reads of the stage) and an
+// MFMA-only phase, group 1 one phase behind group 0.  Outputs leave through
+// LDS as whole rows (the staged epilogues).
 //
 // Workgroup: WM x WN waves, tile BM x BN, MFMA v_mfma_f32_32x32x16_bf16 with
 // fp32 accumulation.  Tile order as in gemm.hip (XCD-aware, grouped rows).
@@ -254,95 +255,6 @@ template <bool KC, int BK>
 __device__ __forceinline__ u32x4 frag(uint32_t tile, int row, int s, int lane) {
   if constexpr (KC) return frag_kc<BK>(tile, row + (lane & 31), s, lane >> 5);
   else return frag_mn<BK>(tile, row, s, lane);
-}
-
-// MFMA over one stage (BK / 16 k-steps), fragments of step s+1 read while step
-// s multiplies.
-template <int FM, int FN, int BK, bool AKC, bool BKC, typename Hook>
-__device__ __forceinline__ void mma_stage(const char* ta_p, const char* tb_p, int wm0, const int (&bcol)[FN],
-                                          f32x16 (&acc)[FM][FN], const Hook& after_step) {
-  constexpr int STEPS = BK / 16;
-  constexpr int READS = FM * (AKC ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS reads per step
-  const uint32_t ta = lds_addr(ta_p), tb = lds_addr(tb_p);
-  const int lane = threadIdx.x & 63;
-  u32x4 af[2][FM], bfr[2][FN];
-  auto fetch = [&](int s, int buf) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af[buf][i] = frag<AKC, BK>(ta, wm0 + i * 32, s, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[buf][j] = frag<BKC, BK>(tb, bcol[j], s, lane);
-  };
-  fetch(0, 0);
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    // keep the reads of step s+1 ahead of the MFMAs of step s
-    if (s + 1 < STEPS) {
-      fetch(s + 1, (s + 1) & 1);
-      wait_lgkmcnt<(READS < 15 ? READS : 15)>();  // conservative when the count saturates
-    } else {
-      wait_lgkmcnt<0>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfr[s & 1][j]),
-                                                            __builtin_bit_cast(bf16x8, af[s & 1][i]),
-                                                            acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // work slotted between the steps (the next stage's global->LDS loads):
-    // spreading it keeps the MFMA pipe fed while the load path is busy
-    after_step(s);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The pipelined K loop shared by both kernels.  issue(stage, kt, q0, q1)
-// issues loads [q0, q1) of stage kt (Q per wave); compute(stage, hook) runs
-// the MFMAs of a stage and calls hook(s) after k-step s, where a share of the
-// next stage's loads is issued.
-template <int NS, int STAGE_BYTES, int Q, int STEPS, typename Issue, typename Compute>
-__device__ __forceinline__ void k_loop(char* smem, int nk, const Issue& issue, const Compute& compute) {
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(smem + s * STAGE_BYTES, s, 0, Q);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(NS - 2, nk - 1 - kt);
-    wait_vmcnt_dyn(ahead * Q);
-    barrier();
-    const int next = kt + NS - 1;
-    char* next_stage = smem + (next % NS) * STAGE_BYTES;
-    compute(smem + (kt % NS) * STAGE_BYTES, [&](int s) {
-      if (next < nk) issue(next_stage, next, s * Q / STEPS, (s + 1) * Q / STEPS);
-    });
-  }
-}
-
-// Warp-specialised K loop: producer waves only issue the global->LDS loads,
-// consumer waves only read fragments and run MFMAs; both meet at one barrier
-// per stage.  A producer stalled on a busy load path then never holds back
-// the MFMA pipe of its SIMD.
-template <int NS, int STAGE_BYTES, int Q, typename Issue, typename Compute>
-__device__ __forceinline__ void k_loop_split(char* smem, int nk, bool producer, const Issue& issue,
-                                             const Compute& compute) {
-  if (producer) {
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < nk) issue(smem + s * STAGE_BYTES, s, 0, Q);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(NS - 2, nk - 1 - kt);
-      wait_vmcnt_dyn(ahead * Q);
-      barrier();
-      const int next = kt + NS - 1;
-      if (next < nk) issue(smem + (next % NS) * STAGE_BYTES, next, 0, Q);
-    }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) {
-      barrier();
-      compute(smem + (kt % NS) * STAGE_BYTES, [](int) {});
-    }
-  }
 }
 
 // Fragments of one whole stage, read ahead of the MFMAs that use them.
@@ -660,10 +572,10 @@ constexpr int kEpiPartial = 100;
 // FWD / DGRAD: rows split by group.  A = activation rows (K-contiguous).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
-__global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows_kernel(Args a) {
-  constexpr int NC = WM * WN;                 // consumer (MFMA) waves
-  constexpr int NW = NP > 0 ? NP : NC;        // waves issuing loads
-  constexpr int W0 = NP > 0 ? NC : 0;         // first loading wave
+__global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
+  static_assert(NP == kPingPong, "the ping-pong schedule is the one built");
+  constexpr int NC = WM * WN;                 // waves: every wave loads and multiplies
+  constexpr int NW = NC, W0 = 0;
   constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr bool PAIR = (EPI == gemm::EPI_SWIGLU_FWD);
   constexpr bool BKC = (KIND == gemm::KIND_DGRAD);
@@ -696,15 +608,11 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
   }
 
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool producer = NP > 0 && wave_u >= NC;
-  const bool loads = NP <= 0 || producer;
   Loader<BM, BK, true, NW, W0> la;
   Loader<BN, BK, BKC, NW, W0> lb;
-  if (loads) {
-    la.init_kc(a.lda);
-    if constexpr (BKC) lb.init_kc(a.ldb);
-    else lb.init_mn(a.ldb, PAIR, N - n0);
-  }
+  la.init_kc(a.lda);
+  if constexpr (BKC) lb.init_kc(a.ldb);
+  else lb.init_mn(a.ldb, PAIR, N - n0);
   const bool split = BKC && a.b_split > 0;
 
   constexpr int QA = Loader<BM, BK, true, NW, W0>::PER, QB = Loader<BN, BK, BKC, NW, W0>::PER;
@@ -743,21 +651,11 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((K + BK - 1) / BK);
-  auto compute = [&](const char* st, const auto& hook) {
-    mma_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, acc, hook);
-  };
-  if constexpr (NP == kPingPong) {
-    StageFrags<FM, FN, BK> fr;
-    k_loop_pingpong<NS, STAGE, QA + QB>(
-        smem, nk, wave_u / (NC / 2), issue,
-        [&](const char* st) { read_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, fr); },
-        [&]() { mma_frags<FM, FN, BK>(fr, acc); });
-  } else if constexpr (NP > 0) {
-    k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
-    if (producer) return;
-  } else {
-    k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
-  }
+  StageFrags<FM, FN, BK> fr;
+  k_loop_pingpong<NS, STAGE, QA + QB>(
+      smem, nk, wave_u / (NC / 2), issue,
+      [&](const char* st) { read_stage<FM, FN, BK, true, BKC>(st, st + A_BYTES, wm0, bcol, fr); },
+      [&]() { mma_frags<FM, FN, BK>(fr, acc); });
 
   if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
                 (EPI == gemm::EPI_STORE || EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD))
@@ -773,10 +671,10 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_rows
 // WGRAD: C_g[M, N] = X[rows_g, M]^T . D[rows_g, N], both MN-contiguous.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
-__global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgrad_kernel(Args a) {
+__global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
+  static_assert(NP == kPingPong, "the ping-pong schedule is the one built");
   constexpr int NC = WM * WN;
-  constexpr int NW = NP > 0 ? NP : NC;
-  constexpr int W0 = NP > 0 ? NC : 0;
+  constexpr int NW = NC, W0 = 0;
   constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -818,13 +716,10 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
   ra.init(X + (r0 * a.lda + m0) * 2, Kr * a.lda * 2 - m0 * 2);
   rb.init(D + (r0 * a.ldb + n0) * 2, Kr * a.ldb * 2 - n0 * 2);
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool producer = NP > 0 && wave_u >= NC;
   Loader<BM, BK, false, NW, W0> la;
   Loader<BN, BK, false, NW, W0> lb;
-  if (NP <= 0 || producer) {
-    la.init_mn(a.lda, false, M - m0);
-    lb.init_mn(a.ldb, false, N - n0);
-  }
+  la.init_mn(a.lda, false, M - m0);
+  lb.init_mn(a.ldb, false, N - n0);
   constexpr int QA = Loader<BM, BK, false, NW, W0>::PER, QB = Loader<BN, BK, false, NW, W0>::PER;
   auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
@@ -850,21 +745,11 @@ __global__ __launch_bounds__(64 * (WM * WN + (NP > 0 ? NP : 0))) void gemm3_wgra
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (int)((Kr + BK - 1) / BK);
-  auto compute = [&](const char* st, const auto& hook) {
-    mma_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, acc, hook);
-  };
-  if constexpr (NP == kPingPong) {
-    StageFrags<FM, FN, BK> fr;
-    k_loop_pingpong<NS, STAGE, QA + QB>(
-        smem, nk, wave_u / (NC / 2), issue,
-        [&](const char* st) { read_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, fr); },
-        [&]() { mma_frags<FM, FN, BK>(fr, acc); });
-  } else if constexpr (NP > 0) {
-    k_loop_split<NS, STAGE, QA + QB>(smem, nk, producer, issue, compute);
-    if (producer) return;
-  } else {
-    k_loop<NS, STAGE, QA + QB, BK / 16>(smem, nk, issue, compute);
-  }
+  StageFrags<FM, FN, BK> fr;
+  k_loop_pingpong<NS, STAGE, QA + QB>(
+      smem, nk, wave_u / (NC / 2), issue,
+      [&](const char* st) { read_stage<FM, FN, BK, false, false>(st, st + A_BYTES, wm0, bcol, fr); },
+      [&]() { mma_frags<FM, FN, BK>(fr, acc); });
 
   if constexpr (SPLIT) {
     // fp32 partial of this split: [split][weight set][M][N]
@@ -924,7 +809,7 @@ hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
   auto kern = gemm3_rows_kernel<BM, BN, WM, WN, BK, NS, NP, KIND, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + (NP > 0 ? NP : 0))), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
   return hipGetLastError();
 }
 
@@ -939,7 +824,7 @@ hipError_t launch_wgrad(Args a, hipStream_t st) {
   auto kern = gemm3_wgrad_kernel<BM, BN, WM, WN, BK, NS, NP, EPI>;
   static hipError_t prep = prepare_lds(kern, lds);
   if (prep != hipSuccess) return prep;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * (WM * WN + (NP > 0 ? NP : 0))), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, st, a);
   return hipGetLastError();
 }
 
