@@ -196,14 +196,13 @@ __device__ __forceinline__ void store_cols(T* p, const float (&v)[CPT]) {
 // time.  The tokens' row indices and dlogits are the same for the whole wave
 // and come in through scalar loads; the gathered rows of both tokens are
 // loaded before they are summed.
-template <typename T, int EP, int CPT, bool FULL, int KMAX>
+template <typename T, int EP, int CPT, bool FULL, int KMAX, int TU, bool ADD>
 __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__ dx_perm,
                                                            const int32_t* __restrict__ row_of,
                                                            const float* __restrict__ dl, const T* __restrict__ w_r,
                                                            const T* __restrict__ dx_add, T* __restrict__ dx,
                                                            int64_t Tn, int d, int E, int k, int tpw) {
   static_assert(CPT * EP == 64, "64 router weights per lane");
-  constexpr int TU = 2;  // tokens per round
   const int64_t t0 = (int64_t)blockIdx.x * tpw;
   const int i0 = (blockIdx.y * 256 + threadIdx.x) * CPT;
   const bool col_ok = i0 < d;  // d is a multiple of 8: a lane's CPT columns are all in or all out
@@ -252,8 +251,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
         const bool ok = col_ok && rows[u][j] >= 0;
         load_cols_if<T, CPT>(ok, dx_perm + (int64_t)(ok ? rows[u][j] : 0) * d + i0, dx_perm, g[u][j]);
       }
-      const bool aok = dx_add != nullptr && col_ok;
-      load_cols_if<T, CPT>(aok, (aok ? dx_add : dx_perm) + (aok ? tt[u] * d + i0 : 0), dx_perm, add[u]);
+      if constexpr (ADD) load_cols_if<T, CPT>(col_ok, dx_add + (col_ok ? tt[u] * d + i0 : 0), dx_add, add[u]);
     }
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
@@ -273,8 +271,10 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const T* __restrict__
       }
       // one token's dlogits at a time in scalar registers (up to 64)
       if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ADD) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] += add[u][c];
+        for (int c = 0; c < CPT; ++c) acc[c] += add[u][c];
+      }
       if (col_ok && tb + u <= tlast) store_cols<T, CPT>(dx + tt[u] * d + i0, acc);
     }
   }
@@ -462,9 +462,16 @@ static hipError_t launch_dbwd_k(const DispatchBwdArgs& a, hipStream_t st) {
   const int64_t bx = (a.T + TPW - 1) / TPW;
   const int by = (int)((a.d + 256 * CPT - 1) / (256 * CPT));
   if (bx <= 0) return hipSuccess;
-  auto kern = a.E == EP ? dispatch_bwd_kernel<T, EP, CPT, true, KMAX> : dispatch_bwd_kernel<T, EP, CPT, false, KMAX>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)bx, by), dim3(256), 0, st, (const T*)a.dx_perm, a.row_of, a.dlogits,
-                     (const T*)a.w_router, (const T*)a.dx_add, (T*)a.dx, a.T, (int)a.d, a.E, a.k, TPW);
+  // two tokens per round (4 and 8 measured slower: more registers, fewer
+  // waves); the shared-expert dx is added only when there is one
+#define MOE_DBWD(ADD)                                                                                              \
+  hipLaunchKernelGGL((a.E == EP ? dispatch_bwd_kernel<T, EP, CPT, true, KMAX, 2, ADD>                             \
+                                : dispatch_bwd_kernel<T, EP, CPT, false, KMAX, 2, ADD>),                          \
+                     dim3((unsigned)bx, by), dim3(256), 0, st, (const T*)a.dx_perm, a.row_of, a.dlogits,           \
+                     (const T*)a.w_router, (const T*)a.dx_add, (T*)a.dx, a.T, (int)a.d, a.E, a.k, TPW)
+  if (a.dx_add != nullptr) MOE_DBWD(true);
+  else MOE_DBWD(false);
+#undef MOE_DBWD
   return hipGetLastError();
 }
 

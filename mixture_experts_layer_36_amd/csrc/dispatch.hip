@@ -7,16 +7,18 @@
 // pos = number of tokens t' < t that chose the same expert; it is kept iff
 // pos < C, so overflow is dropped in token order.
 //
-// Stable positions without order-dependent atomics, in four launches:
+// Stable positions without order-dependent atomics, in three launches (four
+// for inputs of more than kFusedScanBlocks blocks, where a one-workgroup
+// scan kernel replaces the per-workgroup sums of step 2):
 //   1. block_hist: per block of 256 tokens, count the tokens choosing each
 //      expert (integer LDS atomics: the count does not depend on order);
-//   2. scan: one workgroup (wave prefix sums) turns the block counts into
-//      per-(block, expert) bases, raw / kept counts, slot offsets and send
-//      segments;
-//   3. rows: per block, each token's rank among the block's earlier tokens
-//      (64-bit wave ballots + popcount, then a prefix over the 4 waves) gives
-//      pos, the kept flag, the row, row_of and assign_of_row;
-//   4. copy: each kept token row is read once and written to its <= k rows
+//   2. rows: per block, the sums of the block counts before it and in all
+//      (each workgroup reduces them itself, so no separate scan launch) give
+//      the per-expert bases, raw / kept counts, slot offsets and send
+//      segments; each token's rank among the block's earlier tokens (64-bit
+//      wave ballots + popcount, then a prefix over the 4 waves) gives pos, the
+//      kept flag, the row, row_of and assign_of_row;
+//   3. copy: each kept token row is read once and written to its <= k rows
 //      (16-byte loads / stores, coalesced along the row).
 #include "common.h"
 #include "kernels.h"
@@ -56,7 +58,8 @@ __device__ __forceinline__ V wave_incl_scan(V v, int lane) {
   return v;
 }
 
-// One workgroup of 16 waves.  Wave w scans the block-count columns of experts
+// Many blocks (nb > kFusedScanBlocks): one workgroup of 16 waves scans the
+// block counts once for all.  Wave w scans the block-count columns of experts
 // w, w + 16, ...: 64 blocks per round, one per lane, by a wave prefix sum plus
 // the carry of the earlier rounds (block_base = exclusive prefix down the
 // column).  Then wave 0 takes one slot per lane for the prefix over the kept
@@ -111,20 +114,62 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   }
 }
 
+// Positions and rows, one workgroup per block of kDispatchBlock tokens.
+//  a. Each workgroup reduces the block counts itself (nb x E integers that
+//     every workgroup reads, from L2): base[e] = tokens of earlier blocks that
+//     chose expert e, raw[e] = all of them; kept[e] = min(raw[e], C).  Thread
+//     tid adds expert tid % E over the blocks tid / E, tid / E + G, ... and
+//     wave 0 sums the G partials of each expert.
+//  b. Wave 0 turns the kept counts into slot offsets (a wave prefix sum in
+//     slot order), hence each expert's first row; workgroup 0 also writes the
+//     counts, the slot offsets and the send segments.
+//  c. Each token's rank among the block's earlier tokens choosing the same
+//     expert (64-bit wave ballots + popcount, then a prefix over the waves)
+//     gives pos = base + rank, the kept flag (pos < C) and the row.
+// Every workgroup reading every block count costs nb^2 E reads in all, so
+// with more than kFusedScanBlocks blocks (FUSED = false) a and b come from the
+// scan kernel's block_base and expert_start instead.
+constexpr int kFusedScanBlocks = 128;
+
+template <bool FUSED>
 __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
-    const int32_t* __restrict__ idx, int64_t Tn, int E, int k, int64_t C, const int32_t* __restrict__ block_base,
+    const int32_t* __restrict__ idx, int64_t Tn, int E, int k, int64_t C, int R, int placement,
+    const int32_t* __restrict__ block_counts, int nb, int32_t* __restrict__ raw_counts,
+    int32_t* __restrict__ kept_counts, int64_t* __restrict__ slot_offsets, int32_t* __restrict__ send_counts,
+    int64_t* __restrict__ send_offsets, const int32_t* __restrict__ block_base,
     const int64_t* __restrict__ expert_start, int32_t* __restrict__ row_of, int32_t* __restrict__ assign_of_row) {
-  constexpr int NW = kDispatchBlock / 64;
+  constexpr int NT = kDispatchBlock, NW = NT / 64;
+  __shared__ int pre_s[NT], tot_s[NT];
+  __shared__ int base_s[64];
+  __shared__ int64_t start_s[64];
   __shared__ int wave_cnt[NW][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kDispatchBlock + tid;
+  const int b = blockIdx.x;
+  const int64_t t = (int64_t)b * NT + tid;
   int my_e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) my_e[j] = (j < k && t < Tn) ? idx[t * k + j] : -1;
+
+  // a. partial sums of the block counts (E <= 64, so G >= 4)
+  const int G = NT / E;
+  if (FUSED) {
+    int pre = 0, tot = 0;
+    if (tid < G * E) {
+      const int e = tid % E;
+      for (int bb = tid / E; bb < nb; bb += G) {
+        const int v = block_counts[(int64_t)bb * E + e];
+        tot += v;
+        pre += bb < b ? v : 0;
+      }
+    }
+    pre_s[tid] = pre;
+    tot_s[tid] = tot;
+  }
+
+  // c (first half). ranks within the wave, and the wave's count per expert
   int rank[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    my_e[j] = (j < k && t < Tn) ? idx[t * k + j] : -1;
-    rank[j] = 0;
-  }
+  for (int j = 0; j < 8; ++j) rank[j] = 0;
   const unsigned long long lt = (1ull << lane) - 1ull;
   for (int e = 0; e < E; ++e) {
     bool c = false;
@@ -138,6 +183,54 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
     if (lane == 0) wave_cnt[w][e] = __popcll(mask);
   }
   __syncthreads();
+
+  // a (end) and b. wave 0: lane e holds expert e's base and raw count; lane s
+  // holds slot s for the prefix in slot order
+  if (!FUSED) {
+    if (tid < E) {
+      base_s[tid] = block_base[(int64_t)b * E + tid];
+      start_s[tid] = expert_start[tid];
+    }
+  } else if (w == 0) {
+    int base = 0, raw = 0;
+    if (lane < E) {
+      for (int g = 0; g < G; ++g) {
+        base += pre_s[g * E + lane];
+        raw += tot_s[g * E + lane];
+      }
+      base_s[lane] = base;
+    }
+    const int64_t kept = lane < E ? (raw < C ? raw : C) : 0;
+    const int ex = lane < E ? slot_expert(lane, E, R, placement) : 0;
+    const int64_t v = __shfl(kept, ex, 64);  // kept count of slot lane's expert
+    const int64_t sv = lane < E ? v : 0;
+    const int64_t incl = wave_incl_scan(sv, lane), excl = incl - sv;
+    const int64_t total = __shfl(incl, 63, 64);
+    if (lane < E) start_s[ex] = excl;
+    if (b == 0) {
+      if (lane < E) {
+        raw_counts[lane] = raw;
+        kept_counts[lane] = (int32_t)kept;
+        slot_offsets[lane] = excl;
+      }
+      // send segment q = lane < R: slots [q L, (q + 1) L)
+      const int L = E / R;
+      const int s0 = lane < R ? lane * L : 0, s1 = lane < R ? (lane + 1) * L : 0;
+      const int64_t o0 = __shfl(excl, s0 & 63, 64);
+      const int64_t o1 = s1 < E ? __shfl(excl, s1 & 63, 64) : total;
+      if (lane < R) {
+        send_offsets[lane] = o0;
+        send_counts[lane] = (int32_t)(o1 - o0);
+      }
+      if (lane == 0) {
+        slot_offsets[E] = total;
+        send_offsets[R] = total;
+      }
+    }
+  }
+  __syncthreads();
+
+  // c (end). position, kept flag and row of each of the token's choices
   if (t >= Tn) return;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -147,9 +240,9 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
     if (e >= 0 && e < E) {
       int prefix = 0;
       for (int ww = 0; ww < w; ++ww) prefix += wave_cnt[ww][e];
-      const int64_t pos = (int64_t)block_base[(int64_t)blockIdx.x * E + e] + prefix + rank[j];
+      const int64_t pos = (int64_t)base_s[e] + prefix + rank[j];
       if (pos < C) {
-        row = (int32_t)(expert_start[e] + pos);
+        row = (int32_t)(start_s[e] + pos);
         assign_of_row[row] = (int32_t)(t * k + j);
       }
     }
@@ -231,14 +324,22 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t s
                      a.block_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64 * kScanWaves), 0, st, a.block_counts, nb, a.E, a.C, a.R,
-                     a.placement,
-                     a.block_base, a.raw_counts, a.expert_counts, a.expert_offsets, a.send_counts, a.send_offsets,
-                     a.expert_start);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_rows_kernel, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E, a.k, a.C,
-                     a.block_base, a.expert_start, a.row_of, a.assign_of_row);
+  if (nb <= kFusedScanBlocks) {
+    hipLaunchKernelGGL(dispatch_rows_kernel<true>, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E,
+                       a.k, a.C, a.R, a.placement, a.block_counts, nb, a.raw_counts, a.expert_counts,
+                       a.expert_offsets, a.send_counts, a.send_offsets, nullptr, nullptr, a.row_of,
+                       a.assign_of_row);
+  } else {
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64 * kScanWaves), 0, st, a.block_counts, nb, a.E, a.C, a.R,
+                       a.placement, a.block_base, a.raw_counts, a.expert_counts, a.expert_offsets, a.send_counts,
+                       a.send_offsets, a.expert_start);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(dispatch_rows_kernel<false>, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E,
+                       a.k, a.C, a.R, a.placement, a.block_counts, nb, a.raw_counts, a.expert_counts,
+                       a.expert_offsets, a.send_counts, a.send_offsets, a.block_base, a.expert_start, a.row_of,
+                       a.assign_of_row);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (bf16_dtype) launch_permute_copy<bf16>(a, st);

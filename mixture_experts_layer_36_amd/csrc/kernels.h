@@ -20,7 +20,7 @@ struct DispatchArgs {
   int32_t* raw_counts; int32_t* expert_counts; int64_t* expert_offsets;
   int32_t* send_counts; int64_t* send_offsets;
   // workspace
-  int32_t* block_counts; int32_t* block_base; int64_t* expert_start;
+  int32_t* block_counts; int32_t* block_base; int64_t* expert_start;  // the last two: many blocks only
   int64_t T; int64_t d; int E; int k; int64_t C; int R; int placement;
 };
 

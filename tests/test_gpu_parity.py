@@ -105,6 +105,10 @@ FUZZ = {
                              seed=27),
     "T8192_E2_splitk": W("T8192_E2_splitk", T=8192, d=64, ffn=48, E=2, k=1, capacity_factor=0.0,
                          gating="softmax_topk", act="gelu", dtype="bf16", seed=28),
+    # more than 128 blocks of 256 tokens: dispatch takes its separate scan
+    # launch instead of the per-workgroup sums of the block counts
+    "T40000_E64_scan": W("T40000_E64_scan", T=40000, d=32, ffn=16, E=64, k=6, capacity_factor=1.0,
+                         gating="softmax_topk", act="gelu", dtype="bf16", ep_ranks=8, seed=29),
 }
 
 
