@@ -8,8 +8,9 @@
 //   RENORM / TOPK_SOFTMAX: the weights are a softmax over the chosen logits:
 //                          dl[e_j] = g_j * (dg_j - sum_m g_m dg_m), 0 elsewhere
 // router wgrad: dW_r = x^T dl as a deterministic two-stage reduction over
-//   tokens: each block of tokens writes an fp32 partial [d, E], then the
-//   partials are summed in block order (at most 64 blocks).
+//   tokens: each block of tokens writes an fp32 partial [d, E] (vector units,
+//   bf16 MFMA or fp32 MFMA by dtype and E), then the partials are summed in
+//   block order (at most 64 blocks).
 #include "common.h"
 #include "kernels.h"
 
@@ -335,15 +336,176 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// partial[b][i][e] on the bf16 matrix cores (bf16 x, more than 16 experts):
+// v_mfma_f32_16x16x32_bf16 with M = 16 columns of x, N = 16 experts and K =
+// 32 tokens.  dlogits enter as bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi),
+// one MFMA each), which keeps about 16 significant bits; products of bf16
+// values are exact in the fp32 accumulators.  Both operands are token-major
+// in memory, so each 32-token step stages x[32][256 columns] and hi / lo
+// [32][EP] in LDS (two buffers, one barrier per step: a buffer is rewritten
+// only after every wave has passed the barrier that follows its last reads),
+// and the fragments come out transposed by ds_read_b64_tr_b16: within a
+// 16-lane group, lane j addresses 4 consecutive columns of K row j / 4 of a
+// 4 x 16 block and lane i receives column i's 4 K values, so two reads give a
+// lane the 8 consecutive tokens of its MFMA operand.  A workgroup of 4 waves
+// owns 256 columns (64 per wave) for all experts and tb tokens; the next
+// step's global loads are in flight while the current one is multiplied.
+constexpr int kRwbCols = 256;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const __attribute__((address_space(3))) char*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int EP>
+__global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* __restrict__ x,
+                                                                   const float* __restrict__ dl,
+                                                                   float* __restrict__ partial, int64_t Tn, int d,
+                                                                   int E, int tb) {
+  constexpr int NB = EP / 16;
+  constexpr int XP = kRwbCols * 2 + 32;  // x tile row pitch in bytes: the +32 puts the 4 K rows of a read on other banks
+  constexpr int DP = EP * 2 + 32;        // hi / lo tile row pitch
+  constexpr int XB = 32 * XP, DB = 32 * DP, BUF = XB + 2 * DB;
+  constexpr int DQ = EP / 4, DR = 256 / DQ, DPASS = 32 / DR;  // dlogits: 4 experts per thread, DR rows per pass
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * kRwbCols;
+  const int64_t tbeg = (int64_t)blockIdx.y * tb;
+  const int64_t tend = tbeg + tb < Tn ? tbeg + tb : Tn;
+  const int nsteps = tend > tbeg ? (int)((tend - tbeg + 31) / 32) : 0;
+
+  // global -> registers for one step: x rows tid / 32 + 8 p, 16-byte chunk
+  // tid % 32; dlogits rows tid / DQ + DR p, experts 4 (tid % DQ) .. + 3
+  // (unconditional loads from valid addresses, zeros by select)
+  const int xcol = c0 + (tid & 31) * 8;
+  const bool xcol_ok = xcol < d;  // d is a multiple of 8: a chunk is all in or all out
+  const int de = 4 * (tid % DQ);
+  u32x4 xr[4];
+  float dv[DPASS][4];
+  auto gload = [&](int s) {
+    const int64_t t0 = tbeg + 32 * s;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t t = t0 + (tid >> 5) + 8 * p;
+      const bool ok = xcol_ok && t < tend;
+      const u32x4 v = ld16(x + (t < tend ? t : tbeg) * d + (xcol_ok ? xcol : 0));
+      xr[p] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int p = 0; p < DPASS; ++p) {
+      const int64_t t = t0 + tid / DQ + DR * p;
+      const int64_t tc = t < tend ? t : tbeg;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = t < tend && de + q < E;
+        const float v = dl[tc * E + (de + q < E ? de + q : 0)];
+        dv[p][q] = ok ? v : 0.0f;
+      }
+    }
+  };
+  auto lwrite = [&](char* buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) st16(buf + ((tid >> 5) + 8 * p) * XP + (tid & 31) * 16, xr[p]);
+#pragma unroll
+    for (int p = 0; p < DPASS; ++p) {
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = bf16_bits(dv[p][q]);
+        l[q] = bf16_bits(dv[p][q] - __uint_as_float(h[q] << 16));
+      }
+      const int off = (tid / DQ + DR * p) * DP + de * 2;
+      *reinterpret_cast<u32x2*>(buf + XB + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(buf + XB + DB + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    }
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // this lane's transposing-read address in a tile: K row 8 G + 4 r + j / 4,
+  // column 4 (j % 4) of the 16-column block (G = lane / 16, j = lane % 16)
+  const int G = lane >> 4, j = lane & 15;
+  const int kr = 8 * G + (j >> 2), cq = 4 * (j & 3);
+  if (nsteps > 0) gload(0);
+  for (int s = 0; s < nsteps; ++s) {
+    char* buf = lds + (s & 1) * BUF;
+    lwrite(buf);
+    __syncthreads();
+    if (s + 1 < nsteps) gload(s + 1);
+    u32x4 a[4], bh[NB], bl[NB];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const char* pa = buf + kr * XP + (64 * wave + 16 * mb + cq) * 2;
+      const u32x2 r0 = lds_read_tr16(pa), r1 = lds_read_tr16(pa + 4 * XP);
+      a[mb] = u32x4{r0[0], r0[1], r1[0], r1[1]};
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const char* ph = buf + XB + kr * DP + (16 * nb + cq) * 2;
+      const u32x2 h0 = lds_read_tr16(ph), h1 = lds_read_tr16(ph + 4 * DP);
+      const u32x2 l0 = lds_read_tr16(ph + DB), l1 = lds_read_tr16(ph + DB + 4 * DP);
+      bh[nb] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+      bl[nb] = u32x4{l0[0], l0[1], l1[0], l1[1]};
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[mb]),
+                                                              __builtin_bit_cast(bf16x8_t, bh[nb]), acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[mb]),
+                                                              __builtin_bit_cast(bf16x8_t, bl[nb]), acc[mb][nb], 0, 0, 0);
+      }
+  }
+  // accumulator (mb, nb)[q] of lane l: column 64 wave + 16 mb + 4 (l / 16) + q, expert 16 nb + l % 16
+  float* pb = partial + (int64_t)blockIdx.y * d * E;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = c0 + 64 * wave + 16 * mb + 4 * G + q, e = 16 * nb + j;
+        if (i < d && e < E) pb[(int64_t)i * E + e] = acc[mb][nb][q];
+      }
+}
+
+template <int EP>
+static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
+  const int nb = router_wgrad_blocks(a.T);
+  const int tb = (int)((a.T + nb - 1) / nb);  // tokens per block
+  const dim3 grid((unsigned)((a.d + kRwbCols - 1) / kRwbCols), nb);
+  hipLaunchKernelGGL((router_wgrad_bf16mfma_kernel<EP>), grid, dim3(256), 0, st, (const bf16*)a.x, a.dlogits,
+                     a.partial, a.T, (int)a.d, a.E, tb);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t dE = a.d * a.E;
+  hipLaunchKernelGGL((router_wgrad_reduce_kernel<bf16>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
+                     a.partial, nb, dE, (bf16*)a.dw_router);
+  return hipGetLastError();
+}
+
 // bf16 x with up to 16 experts: the vector kernel, bound by reading x (the
 // fp32 MFMA pads E to 16 and measured slower on the Mixtral shape, 0.059
-// against 0.049 ms for the whole router backward).  More experts, or fp32 x:
-// the fp32 MFMA kernel (DeepSeek-V2-Lite shape 0.187 -> 0.137 ms).
+// against 0.049 ms for the whole router backward).  bf16 x with more experts:
+// the bf16 MFMA kernel with dlogits as hi + lo (DeepSeek-V2-Lite shape: 0.14
+// ms on the fp32 MFMA kernel, 0.05 ms).  fp32 x: the fp32 MFMA kernel.
 template <typename T>
 static hipError_t launch_rwg_dt(const RouteBwdArgs& a, hipStream_t st) {
   if (sizeof(T) == 2 && a.E <= 8) return launch_rwg<T, 8>(a, st);
   if (sizeof(T) == 2 && a.E <= 16) return launch_rwg<T, 16>(a, st);
   if (a.E <= 16) return launch_rwg_mfma<T, 16>(a, st);
+  if constexpr (sizeof(T) == 2) {
+    if (a.E <= 32) return launch_rwg_bf16mfma<32>(a, st);
+    return launch_rwg_bf16mfma<64>(a, st);
+  }
   if (a.E <= 32) return launch_rwg_mfma<T, 32>(a, st);
   return launch_rwg_mfma<T, 64>(a, st);
 }
