@@ -18,6 +18,7 @@ Prints ONE JSON line (stdout):
   kernels     per-entry-point times and achieved rates (events around each call)
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_bf16]
+       [--graph]                (time replays of the step captured in one HIP graph)
        [--calibrate-copy MIB]   (also runs a plain device copy of MIB MiB, for
                                  scaling memory counters in a profiler run)
 """
@@ -132,6 +133,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the whole step captured in one HIP graph instead of eager calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
@@ -170,14 +173,20 @@ def main():
     torch.cuda.synchronize()
 
     # 1) whole steps, events only at the ends
-    log(f"[bench] timing {args.steps} steps")
+    run_step = lambda: layer.step(x, dy, w)  # noqa: E731
+    if args.graph:
+        graph = layer.capture_step(x, dy, w)
+        run_step = graph.replay
+        for _ in range(args.warmup):
+            run_step()
+    log(f"[bench] timing {args.steps} steps" + (" (HIP graph replays)" if args.graph else ""))
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(st)
     for _ in range(args.steps):
-        layer.step(x, dy, w)
+        run_step()
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -262,7 +271,8 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "ffn": wl.ffn, "E": wl.E, "k": wl.k,
                    "capacity_factor": wl.capacity_factor, "gating": wl.gating, "act": wl.act,
                    "n_shared": wl.n_shared, "ffn_shared": wl.ffn_shared, "ep_ranks": wl.ep_ranks,
-                   "rows_kept": n, "parallelism": "single GPU"},
+                   "rows_kept": n, "parallelism": "single GPU",
+                   "launch": "hip graph" if args.graph else "eager"},
         "grouped_gemm_frac_mfma": roofline["frac"],
         "permute_GBps": permute_gbs,
         "roofline": roofline,

@@ -158,3 +158,23 @@ class MoELayer:
     def step(self, x, dy, w: Weights):
         self.forward(x, w)
         self.backward(x, dy, w)
+
+    def capture_step(self, x, dy, w: Weights):
+        """Record one whole step (every entry point, forward and backward) into
+        a HIP graph; replaying it re-runs the step on the same buffers, with
+        one launch from the host instead of one per kernel.  The entry points
+        launch only the library's own kernels (no memory sets, allocations or
+        synchronisation), so the step captures whole.  A first step runs on a
+        side stream before the capture, so that every launcher's one-time
+        set-up (kernel attributes) happens outside it."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step(x, dy, w)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step(x, dy, w)
+        torch.cuda.synchronize()
+        return graph
