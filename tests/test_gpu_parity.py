@@ -105,6 +105,14 @@ FUZZ = {
                              seed=27),
     "T8192_E2_splitk": W("T8192_E2_splitk", T=8192, d=64, ffn=48, E=2, k=1, capacity_factor=0.0,
                          gating="softmax_topk", act="gelu", dtype="bf16", seed=28),
+    # wide rows with a ragged tail: the bf16 route walks more than 32 K
+    # blocks per wave (its chunked loop), the router-gradient and un-permute
+    # launches end in a partial column block, and the GEMM reductions over d
+    # end in a partial K step; the fp32 case does the same on the vector route
+    "T96_d8200_bf16": W("T96_d8200_bf16", T=96, d=8200, ffn=48, E=4, k=2, capacity_factor=0.0,
+                        gating="softmax_topk_renorm", act="gelu", dtype="bf16", seed=41),
+    "T70_d4104_E20_f32": W("T70_d4104_E20_f32", T=70, d=4104, ffn=40, E=20, k=3, capacity_factor=1.2,
+                           gating="softmax_topk", act="swiglu", dtype="f32", seed=42),
     # more than 128 blocks of 256 tokens: dispatch takes its separate scan
     # launch instead of the per-workgroup sums of the block counts
     "T40000_E64_scan": W("T40000_E64_scan", T=40000, d=32, ffn=16, E=64, k=6, capacity_factor=1.0,
