@@ -21,7 +21,7 @@ Page references (titles as printed on the pages):
   [FSMOE] FSMoE abstract: token routing, token communication, expert
           computation, expert parallelism as the four MoE modules.
 
-Readings adopted where the pages are silent (each is listed in the design doc):
+Readings adopted where the pages are silent:
   * capacity C = ceil(cf*k*T/E) in double from the fp32 factor, capped at T;
     cf <= 0 means dropless (C = T);
   * overflow is dropped in token order: an expert keeps the C lowest-index
