@@ -667,6 +667,68 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
     rows_epilogue_t<bf16, FM, FN, PAIR, EPI>(a, acc, bcol, wm0, lane, row_begin, row_end, n0, N);
 }
 
+// WGRAD work items (split, group, tile).  The items of groups that have rows
+// come first: they take workgroup ids 0 .. nreal-1, remapped over the XCDs so
+// that consecutive items of a group share one XCD's L2 and the real work
+// spreads over every XCD however many groups are empty (remapping all items
+// put a skewed routing's few busy groups on two or three XCDs).  Items of
+// empty groups, which only write zeros, take the ids after them.  Returns
+// false for a workgroup past the last item.
+__device__ __forceinline__ bool wgrad_item_of(const Args& a, int per_g, int ksplit, int& split, int& g, int& tile,
+                                              int64_t& r0, int64_t& r1) {
+  // the wave reads the offsets 64 groups at a time; ballots count the groups
+  // with rows and find the kth of a kind
+  const int lane = (int)(threadIdx.x & 63);
+  auto load = [&](int gg, int64_t& lo, int64_t& hi) {
+    lo = 0;
+    hi = 0;
+    if (gg < a.groups) {
+      lo = a.offsets[gg];
+      hi = a.offsets[gg + 1];
+    }
+  };
+  int64_t lo0, hi0;  // the first 64 groups, kept for the search below
+  load(lane, lo0, hi0);
+  int nz = __popcll(__ballot(hi0 > lo0));
+  for (int c = 64; c < a.groups; c += 64) {
+    int64_t lo, hi;
+    load(c + lane, lo, hi);
+    nz += __popcll(__ballot(hi > lo));
+  }
+  const int nreal = ksplit * nz * per_g;
+  const int hw = (int)blockIdx.x;
+  const bool real = hw < nreal;
+  const int ng = real ? nz : a.groups - nz;
+  const int lin = real ? xcd_remap(hw, nreal) : hw - nreal;
+  if (ng <= 0 || lin >= ksplit * ng * per_g) return false;
+  split = lin / (ng * per_g);
+  const int rem = lin - split * ng * per_g;
+  int kth = rem / per_g;  // the kth group with (or without) rows
+  tile = rem - kth * per_g;
+  for (int c = 0; c < a.groups; c += 64) {
+    const int gg = c + lane;
+    int64_t lo = lo0, hi = hi0;
+    if (c > 0) load(gg, lo, hi);
+    const uint64_t mask = __ballot(gg < a.groups && (hi > lo) == real);
+    const int n = __popcll(mask);
+    if (kth < n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      const int pos = __ffsll((unsigned long long)__ballot(((mask >> lane) & 1) && below == kth)) - 1;
+      g = c + pos;
+      auto lane_value = [pos](int64_t v) {  // v of lane pos, wave-uniform
+        const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, pos);
+        const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), pos);
+        return (int64_t)(((uint64_t)h << 32) | l);
+      };
+      r0 = lane_value(lo);
+      r1 = lane_value(hi);
+      return true;
+    }
+    kth -= n;
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------------------
 // WGRAD: C_g[M, N] = X[rows_g, M]^T . D[rows_g, N], both MN-contiguous.
 // ---------------------------------------------------------------------------
@@ -680,23 +742,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
   constexpr int STAGE = A_BYTES + B_BYTES;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // EPI_PARTIAL launches split the reduction: block `lin` takes split
-  // lin / (groups * tiles) and writes an fp32 partial
+  // EPI_PARTIAL launches split the reduction: an item (split, group, tile)
+  // writes the fp32 partial of its split
   constexpr bool SPLIT = EPI == kEpiPartial;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int per_g = a.tiles_m * a.tiles_n;
-  int split = 0, t = lin;
-  if constexpr (SPLIT) {
-    split = lin / (per_g * a.groups);
-    t = lin - split * per_g * a.groups;
-    if (split >= a.ksplit) return;
-  }
-  const int g = t / per_g;
-  if (g >= a.groups) return;
+  int split = 0, g = 0, tile = 0;
+  int64_t r0 = 0, r1 = 0;
+  if (!wgrad_item_of(a, per_g, SPLIT ? a.ksplit : 1, split, g, tile, r0, r1)) return;
   int mt, nt;
-  grouped_order(t - g * per_g, a.tiles_m, a.tiles_n, mt, nt, a.gm);
+  grouped_order(tile, a.tiles_m, a.tiles_n, mt, nt, a.gm);
   const int wi = weight_index(g, a.rr_R, a.rr_L);
-  int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
   if constexpr (SPLIT) {
     // split s takes rows [r0 + s*chunk, r0 + (s+1)*chunk) of the group, chunk
     // a multiple of BK; a split past the group's rows keeps an empty range
