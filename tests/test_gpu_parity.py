@@ -105,6 +105,11 @@ FUZZ = {
                              seed=27),
     "T8192_E2_splitk": W("T8192_E2_splitk", T=8192, d=64, ffn=48, E=2, k=1, capacity_factor=0.0,
                          gating="softmax_topk", act="gelu", dtype="bf16", seed=28),
+    # a strong router bias sends every token to experts 0 and 1 (counts 8192,
+    # 8192, 0, 0) while the weight gradients split their reductions in 4: the
+    # real items come first and the empty experts' zero partials after them
+    "T8192_E4_skew_splitk": W("T8192_E4_skew_splitk", T=8192, d=64, ffn=48, E=4, k=2, capacity_factor=0.0,
+                              gating="softmax_topk", act="swiglu", dtype="bf16", zipf_s=1.2, seed=43),
     # wide rows with a ragged tail: the bf16 route walks more than 32 K
     # blocks per wave (its chunked loop), the router-gradient and un-permute
     # launches end in a partial column block, and the GEMM reductions over d
@@ -127,6 +132,8 @@ def test_fuzz(name):
     inp = synth.make_inputs(wl)
     _, ref, errs = run_full_parity(wl, inp)
     print({k: f"{v:.2e}" for k, v in errs.items()}, "n =", ref["layout"]["n"], flush=True)
+    if name == "T8192_E4_skew_splitk":  # the case is what its comment says
+        assert list(np.asarray(ref["layout"]["kept_counts"])) == [8192, 8192, 0, 0]
 
 
 @pytest.mark.parametrize("name,wl", [
