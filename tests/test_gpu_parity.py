@@ -118,6 +118,23 @@ FUZZ = {
                         gating="softmax_topk_renorm", act="gelu", dtype="bf16", seed=41),
     "T70_d4104_E20_f32": W("T70_d4104_E20_f32", T=70, d=4104, ffn=40, E=20, k=3, capacity_factor=1.2,
                            gating="softmax_topk", act="swiglu", dtype="f32", seed=42),
+    # bf16 routing with 8 or 16 experts at model widths from 512 to 8192,
+    # ragged T (down to a single token), the three gating modes and the
+    # router bias; the last case spreads over several hundred workgroups
+    "T333_d512_E8_dot2": W("T333_d512_E8_dot2", T=333, d=512, ffn=32, E=8, k=2, capacity_factor=1.0,
+                           gating="topk_softmax", act="swiglu", dtype="bf16", seed=44),
+    "T70_d1024_E8_dot2": W("T70_d1024_E8_dot2", T=70, d=1024, ffn=16, E=8, k=8, capacity_factor=0.0,
+                           gating="softmax_topk", act="gelu", dtype="bf16", seed=45),
+    "T1000_d2048_E16_dot2": W("T1000_d2048_E16_dot2", T=1000, d=2048, ffn=24, E=16, k=3, capacity_factor=0.0,
+                              gating="softmax_topk_renorm", act="gelu", dtype="bf16", zipf_s=1.2, seed=46),
+    "T257_d8192_E8_dot2": W("T257_d8192_E8_dot2", T=257, d=8192, ffn=16, E=8, k=1, capacity_factor=0.0,
+                            gating="softmax_topk", act="gelu", dtype="bf16", seed=47),
+    "T2500_d4096_E16_dot2": W("T2500_d4096_E16_dot2", T=2500, d=4096, ffn=16, E=16, k=2, capacity_factor=1.1,
+                              gating="topk_softmax", act="swiglu", dtype="bf16", seed=48),
+    "T1_d2048_E8_dot2": W("T1_d2048_E8_dot2", T=1, d=2048, ffn=16, E=8, k=2, capacity_factor=0.0,
+                          gating="softmax_topk", act="gelu", dtype="bf16", seed=49),
+    "T40000_d512_E8_dot2": W("T40000_d512_E8_dot2", T=40000, d=512, ffn=16, E=8, k=2, capacity_factor=1.0,
+                             gating="softmax_topk_renorm", act="gelu", dtype="bf16", zipf_s=1.2, seed=50),
     # more than 128 blocks of 256 tokens: dispatch takes its separate scan
     # launch instead of the per-workgroup sums of the block counts
     "T40000_E64_scan": W("T40000_E64_scan", T=40000, d=32, ffn=16, E=64, k=6, capacity_factor=1.0,
@@ -139,6 +156,11 @@ def test_fuzz(name):
 @pytest.mark.parametrize("name,wl", [
     ("ties_bf16_E8", W("ties_bf16_E8", T=700, d=64, ffn=32, E=8, k=2, capacity_factor=1.0,
                       gating="softmax_topk_renorm", act="gelu", dtype="bf16", seed=31)),
+    # the same with wider rows on the bf16 MFMA route (8 and 16 experts)
+    ("ties_bf16_E8_d512", W("ties_bf16_E8_d512", T=2000, d=512, ffn=16, E=8, k=2, capacity_factor=1.0,
+                           gating="softmax_topk_renorm", act="gelu", dtype="bf16", seed=33)),
+    ("ties_bf16_E16_d1024", W("ties_bf16_E16_d1024", T=1500, d=1024, ffn=16, E=16, k=3, capacity_factor=1.0,
+                             gating="softmax_topk_renorm", act="gelu", dtype="bf16", seed=34)),
     ("ties_f32_E64", W("ties_f32_E64", T=300, d=32, ffn=16, E=64, k=6, capacity_factor=1.5,
                       gating="softmax_topk", act="swiglu", dtype="f32", ep_ranks=4, seed=32)),
 ])
