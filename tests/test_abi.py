@@ -134,6 +134,29 @@ def test_bad_groups_and_alignment_rejected(lib):
     assert lib.moe_combine(cp, odd, fake, fake, None, fake, None) == nat.MOE_ERR_INVALID
 
 
+def test_every_ffn_pointer_must_be_aligned(lib):
+    """The grouped GEMM's direct-to-LDS loads take 16-byte pieces at operand
+    bases plus whole rows, so every tensor of the FFN entry points must be
+    16-byte aligned (and the workspace 256-byte aligned): each pointer,
+    misaligned alone, is rejected before anything reaches the GPU."""
+    c = nat.make_config(64, 64, 64, 8, 2, 1.0, "softmax_topk", "swiglu", "bf16")
+    cp = ctypes.byref(c)
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100002)
+    g = nat.MoeGroups(groups=8, ffn=64, rows_max=128, offsets=fake, use_placement=1)
+    for i in range(7):   # x_rows, w_in, w_up, w_out, act_saved, h, y_rows
+        args = [fake] * 7
+        args[i] = odd
+        assert lib.moe_expert_ffn_fwd(cp, ctypes.byref(g), *args, None) == nat.MOE_ERR_INVALID, i
+    for i in range(13):  # x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in, dw_up, dw_out, ws
+        args = [fake] * 12
+        if i < 12:
+            args[i] = odd
+        else:
+            args[11] = ctypes.c_void_p(0x100010)  # ws: 16- but not 256-byte aligned
+        assert lib.moe_expert_ffn_bwd(cp, ctypes.byref(g), *args, None) == nat.MOE_ERR_INVALID, i
+
+
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-1) == b"invalid argument"
