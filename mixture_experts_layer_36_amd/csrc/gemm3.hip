@@ -668,12 +668,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
 }
 
 // WGRAD work items (split, group, tile).  The items of groups that have rows
-// come first: they take workgroup ids 0 .. nreal-1, remapped over the XCDs so
-// that consecutive items of a group share one XCD's L2 and the real work
-// spreads over every XCD however many groups are empty (remapping all items
-// put a skewed routing's few busy groups on two or three XCDs).  Items of
-// empty groups, which only write zeros, take the ids after them.  Returns
-// false for a workgroup past the last item.
+// come first: they take workgroup ids 0 .. nreal-1, remapped over the XCDs,
+// so the real work covers every XCD however many groups are empty (remapping
+// all items put a skewed routing's few busy groups on two or three XCDs).
+// With groups of similar length, each XCD takes consecutive items, whole
+// groups, which then share its L2.  When the longest group has more than
+// twice the mean rows, whole groups would leave the XCDs that hold the long
+// ones working long after the rest, so each group's tiles go instead to the
+// 8 XCDs in 8 runs of consecutive tiles (a run still shares one XCD's L2).
+// Items of empty groups, which only write zeros, take the ids after the real
+// ones.  Returns false for a workgroup past the last item.
 __device__ __forceinline__ bool wgrad_item_of(const Args& a, int per_g, int ksplit, int& split, int& g, int& tile,
                                               int64_t& r0, int64_t& r1) {
   // the wave reads the offsets 64 groups at a time; ballots count the groups
@@ -687,19 +691,30 @@ __device__ __forceinline__ bool wgrad_item_of(const Args& a, int per_g, int kspl
       hi = a.offsets[gg + 1];
     }
   };
+  // (all of it ballots and scalar values: a launch runs many short workgroups
+  // one after another on each CU, so this prologue must stay a few cycles)
   int64_t lo0, hi0;  // the first 64 groups, kept for the search below
   load(lane, lo0, hi0);
+  const int64_t total = a.offsets[a.groups] - a.offsets[0];  // rows of all groups
   int nz = __popcll(__ballot(hi0 > lo0));
   for (int c = 64; c < a.groups; c += 64) {
     int64_t lo, hi;
     load(c + lane, lo, hi);
     nz += __popcll(__ballot(hi > lo));
   }
+  // skewed: some group holds more than twice the mean rows of the groups with rows
+  bool skewed = __ballot((hi0 - lo0) * nz > 2 * total) != 0;
+  for (int c = 64; c < a.groups; c += 64) {
+    int64_t lo, hi;
+    load(c + lane, lo, hi);
+    skewed = skewed || __ballot((hi - lo) * nz > 2 * total) != 0;
+  }
   const int nreal = ksplit * nz * per_g;
   const int hw = (int)blockIdx.x;
   const bool real = hw < nreal;
   const int ng = real ? nz : a.groups - nz;
-  const int lin = real ? xcd_remap(hw, nreal) : hw - nreal;
+  const int run = skewed && per_g >= 8 ? per_g / 8 : 0;
+  const int lin = !real ? hw - nreal : run > 0 ? run_remap(hw, nreal, run) : xcd_remap(hw, nreal);
   if (ng <= 0 || lin >= ksplit * ng * per_g) return false;
   split = lin / (ng * per_g);
   const int rem = lin - split * ng * per_g;

@@ -39,6 +39,21 @@ __device__ __forceinline__ int xcd_remap(int hw, int num) {
   return base + local;
 }
 
+// Workgroup id -> linear item id, spreading runs of C consecutive items over
+// the XCDs: item run j (items jC .. jC + C - 1) goes whole to XCD j % 8, and
+// each XCD takes its runs in order, so the items of a run keep sharing that
+// XCD's L2 while consecutive runs (the parts of one group) go to different
+// XCDs.  Items past the last whole round of 8 runs fall back to xcd_remap.
+// A bijection on [0, n).
+__device__ __forceinline__ int run_remap(int hw, int n, int C) {
+  const int span = 8 * C;
+  const int n0 = n / span * span;
+  if (hw >= n0) return n0 + xcd_remap(hw - n0, n - n0);
+  const int x = hw & 7, l = hw >> 3;
+  const int rho = l / C, off = l - rho * C;
+  return (rho * 8 + x) * C + off;
+}
+
 // Linear tile id -> (row tile, column tile), walking GM row tiles per column
 // so that concurrently running tiles share panels in L2.
 __device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt, int gm = GM) {

@@ -110,6 +110,12 @@ FUZZ = {
     # real items come first and the empty experts' zero partials after them
     "T8192_E4_skew_splitk": W("T8192_E4_skew_splitk", T=8192, d=64, ffn=48, E=4, k=2, capacity_factor=0.0,
                               gating="softmax_topk", act="swiglu", dtype="bf16", zipf_s=1.2, seed=43),
+    # a skewed routing (the longest expert holds more than twice the mean
+    # rows, one expert is empty) whose weight gradients split their reduction
+    # in 2 and have 8 and 16 tiles per expert: each expert's tiles are spread
+    # over the XCDs in runs, the empty expert's zeros come after them
+    "T8192_E8_skew_runs": W("T8192_E8_skew_runs", T=8192, d=1024, ffn=512, E=8, k=2, capacity_factor=0.0,
+                            gating="softmax_topk", act="swiglu", dtype="bf16", zipf_s=1.2, seed=51),
     # wide rows with a ragged tail: the bf16 route walks more than 32 K
     # blocks per wave (its chunked loop), the router-gradient and un-permute
     # launches end in a partial column block, and the GEMM reductions over d
@@ -151,6 +157,10 @@ def test_fuzz(name):
     print({k: f"{v:.2e}" for k, v in errs.items()}, "n =", ref["layout"]["n"], flush=True)
     if name == "T8192_E4_skew_splitk":  # the case is what its comment says
         assert list(np.asarray(ref["layout"]["kept_counts"])) == [8192, 8192, 0, 0]
+    if name == "T8192_E8_skew_runs":
+        kept = np.asarray(ref["layout"]["kept_counts"])
+        nz = int((kept > 0).sum())
+        assert nz < wl.E and kept.max() * nz > 2 * kept.sum()
 
 
 @pytest.mark.parametrize("name,wl", [
