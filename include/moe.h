@@ -171,7 +171,11 @@ int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,
  *   dx_rows [rows_max, d] = dL/d x_rows;
  *   dw_in, dw_up, dw_out: same shapes and dtype as w_in, w_up, w_out;
  *   weight sets with no rows get exact zeros.
- *   ws: moe_plan's workspace (holds dL/dZ or dL/d[A|B] in dtype). */
+ *   ws: moe_plan's workspace (holds dL/dZ or dL/d[A|B] in dtype, then the
+ *       fp32 partials of weight gradients split over their rows).
+ * Errors: MOE_ERR_INVALID also when the group table would need more
+ *   workspace than moe_plan's workspace_bytes for cfg (a table with more
+ *   groups, rows or hidden width than the routed or shared tables above). */
 int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp,
                        const void* x_rows, const void* w_in, const void* w_up,
                        const void* w_out, const void* act_saved, const void* h,

@@ -289,6 +289,10 @@ int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp, const void*
     if (!aligned16(p)) return MOE_ERR_INVALID;
   if (swiglu && (!aligned16(w_up) || !aligned16(dw_up))) return MOE_ERR_INVALID;
   if ((uintptr_t)ws & 255u) return MOE_ERR_INVALID;
+  // the group table's workspace (dL/d act, then split partials) must fit in
+  // moe_plan's workspace_bytes: the routed and shared tables always do
+  if (ffn_bwd_ws(cfg, grp->groups, grp->ffn, grp->rows_max) > ws_layout(cfg, plan_n_max(cfg)).total)
+    return MOE_ERR_INVALID;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = cfg->dtype == MOE_BF16
                      ? ffn_bwd<moe::bf16>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,

@@ -157,6 +157,20 @@ def test_every_ffn_pointer_must_be_aligned(lib):
         assert lib.moe_expert_ffn_bwd(cp, ctypes.byref(g), *args, None) == nat.MOE_ERR_INVALID, i
 
 
+def test_ffn_bwd_rejects_group_tables_beyond_the_workspace(lib):
+    """moe_expert_ffn_bwd writes dL/d act (rows_max x m ffn) and split
+    weight-gradient partials into the caller's moe_plan workspace, so a group
+    table needing more than moe_plan's workspace_bytes is rejected on the
+    host, before anything reaches the GPU."""
+    c = nat.make_config(64, 64, 64, 8, 2, 1.0, "softmax_topk", "swiglu", "bf16")
+    cp = ctypes.byref(c)
+    sizes = nat.plan(c)
+    fake = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
+    for g in (nat.MoeGroups(groups=8, ffn=64, rows_max=sizes.n_max * 64, offsets=fake, use_placement=1),
+              nat.MoeGroups(groups=1, ffn=64 * 64, rows_max=sizes.n_max, offsets=fake, use_placement=0)):
+        assert lib.moe_expert_ffn_bwd(cp, ctypes.byref(g), *([fake] * 12), None) == nat.MOE_ERR_INVALID
+
+
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-1) == b"invalid argument"

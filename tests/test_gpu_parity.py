@@ -241,3 +241,69 @@ def test_graph_replay():
         torch.cuda.synchronize()
         for r, t in zip(ref, outs()):
             np.testing.assert_array_equal(bits(t), r)
+
+
+def test_ffn_caller_group_table_of_65():
+    """The grouped FFN through the C ABI with a caller-built table of 65
+    groups, the most the ABI takes (weight set g for group g): one long
+    group, many short ones and every fifth one empty.  The weight-gradient
+    launches then read the group offsets in two chunks of 64 and, the table
+    being skewed, spread the long group's tiles over the XCDs in runs; the
+    empty groups' weight gradients must be exact zeros."""
+    announce("ffn_caller_group_table_of_65")
+    import oracle
+    from mixture_experts_layer_36_amd import _native as nat, api
+
+    G, d, F, rows_max = 65, 512, 512, 4096
+    cfg = nat.make_config(2048, d, F, 64, 2, 0.0, "softmax_topk", "swiglu", "bf16")
+    sizes = nat.plan(cfg)
+    assert sizes.n_max == rows_max
+    rng = np.random.default_rng(52)
+    counts = rng.integers(1, 60, G)
+    counts[0] = 1500
+    counts[1::5] = 0
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    assert off[-1] <= rows_max and counts.max() * (counts > 0).sum() > 2 * counts.sum()
+
+    x = synth.tensors.normal(61, (rows_max, d), "bf16")
+    dy = synth.tensors.normal(62, (rows_max, d), "bf16")
+    w_in = synth.tensors.normal(63, (G, d, F), "bf16", 0.05)
+    w_up = synth.tensors.normal(64, (G, d, F), "bf16", 0.05)
+    w_out = synth.tensors.normal(65, (G, F, d), "bf16", 0.05)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device="cuda")
+    xd, dyd, wi, wu, wo = dev(x), dev(dy), dev(w_in), dev(w_up), dev(w_out)
+    act, h, y, dx = bf(rows_max, 2 * F), bf(rows_max, F), bf(rows_max, d), bf(rows_max, d)
+    dwi, dwu, dwo = bf(G, d, F), bf(G, d, F), bf(G, F, d)
+    ws = torch.empty(sizes.workspace_bytes, dtype=torch.uint8, device="cuda")
+    offd = torch.from_numpy(off).cuda()
+    grp = api.groups(G, F, rows_max, offd, use_placement=False)
+    api.moe_expert_ffn_fwd(cfg, grp, xd, wi, wu, wo, act, h, y)
+    api.moe_expert_ffn_bwd(cfg, grp, xd, wi, wu, wo, act, h, dyd, dx, dwi, dwu, dwo, ws)
+    torch.cuda.synchronize()
+
+    xf, dyf = oracle.to_f64(x), oracle.to_f64(dy)
+    Wi, Wu, Wo = oracle.to_f64(w_in), oracle.to_f64(w_up), oracle.to_f64(w_out)
+    n = int(off[-1])
+    ref = {k: np.zeros(s) for k, s in (("a", (n, F)), ("b", (n, F)), ("h", (n, F)), ("y", (n, d)),
+                                        ("dx", (n, d)), ("dwi", (G, d, F)), ("dwu", (G, d, F)),
+                                        ("dwo", (G, F, d)))}
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        fw = oracle.expert_ffn_forward(xf[r0:r1], Wi[g], Wo[g], "swiglu", Wu[g])
+        bw = oracle.expert_ffn_backward(xf[r0:r1], dyf[r0:r1], Wi[g], Wo[g], "swiglu", Wu[g])
+        ref["a"][r0:r1], ref["b"][r0:r1], ref["h"][r0:r1], ref["y"][r0:r1] = fw["a"], fw["b"], fw["h"], fw["o"]
+        ref["dx"][r0:r1] = bw["dxp"]
+        ref["dwi"][g], ref["dwu"][g], ref["dwo"][g] = bw["dw_in"], bw["dw_up"], bw["dw_out"]
+    got_act = host(act)[:n]
+    got = {"a": got_act[:, :F], "b": got_act[:, F:], "h": host(h)[:n], "y": host(y)[:n], "dx": host(dx)[:n],
+           "dwi": host(dwi), "dwu": host(dwu), "dwo": host(dwo)}
+    errs = {}
+    for k in ref:
+        e = float(np.max(np.abs(got[k] - ref[k])) / np.max(np.abs(ref[k])))
+        errs[k] = e
+        assert e <= TOL["bf16"], f"{k}: max|err|/max|ref| = {e:.3e}"
+    empty = counts == 0
+    for k in ("dwi", "dwu", "dwo"):
+        assert np.all(got[k][empty] == 0.0), f"{k}: empty groups not exactly zero"
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
