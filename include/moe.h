@@ -108,10 +108,19 @@ typedef struct {
                                uses weight set g                                */
 } moe_groups;
 
-/* Host only.  Capacity, buffer rows and workspace size for cfg.
+/* Host only; no GPU is touched.  Sizes every caller-owned buffer up front,
+ * following the tutorial's 通信优化方法 四 (pre-allocate and reuse buffers
+ * rather than allocating per step): the expert capacity C (Piper 方法论 1
+ * names it a per-GPU model input; C = ceil(cf*k*T/E), dropless C = T), the
+ * rows n_max = min(T*k, E*C) of the permuted buffers (the all-to-all send
+ * buffer of All-to-All 二, which holds at most every kept (token, expert)
+ * pair), and the workspace every call below may use.
  * Errors: MOE_ERR_INVALID (null pointer, non-positive sizes, k > E,
  * E % R != 0, unknown enum), MOE_ERR_UNSUPPORTED (E > 64, k > 8, d or ffn
- * not a multiple of 8). */
+ * not a multiple of 8, T*k >= 2^31, or a row of an expert GEMM operand --
+ * d, or the m*ffn columns of [A | B] (m = 2 for SwiGLU, 1 for GELU), or
+ * m*n_shared*ffn_shared -- wider than 8388352 bytes, the most a 256-row tile
+ * of one GEMM buffer resource may span). */
 int moe_plan(const moe_config* cfg, moe_sizes* out);
 
 /* Gate GEMM, softmax and top-k routing (tutorial: 专家并行 二 step 1, the
@@ -191,8 +200,17 @@ int moe_combine(const moe_config* cfg, const void* y_perm,
                 const int32_t* row_of, const float* topk_w,
                 const void* y_shared, void* y, void* stream);
 
-/* Combine backward.  dy_perm[row_of[t*k+j]] = topk_w[t, j] * dy[t];
- * d_topk_w[t, j] = <dy[t], y_perm[row_of[t*k+j]]> (0 if dropped). */
+/* Combine backward (tutorial: 专家并行与数据并行的结合 三.3: in the
+ * backward pass the output gradient is sent back to the device of each
+ * chosen expert; 专家并行 二 step 4 is the forward merge this reverses).
+ * The chain rule of the weighted sum in moe_combine gives:
+ *   dy_perm[row_of[t*k+j]] = topk_w[t, j] * dy[t]   (the expert's upstream
+ *     gradient, written in the send-buffer layout);
+ *   d_topk_w[t, j] = <dy[t], y_perm[row_of[t*k+j]]> (0 if dropped), the
+ *     gate weight's gradient, fp32 accumulation.
+ * Rows of dy_perm outside the kept rows are untouched.
+ * Errors: MOE_ERR_INVALID for a null pointer or a misaligned dy / y_perm /
+ * dy_perm. */
 int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* y_perm,
                     const int32_t* row_of, const float* topk_w, void* dy_perm,
                     float* d_topk_w, void* stream);
@@ -207,10 +225,17 @@ int moe_route_bwd(const moe_config* cfg, const void* x, const float* logits,
                   const int32_t* topk_idx, const float* d_topk_w,
                   float* dlogits, void* dw_router, void* ws, void* stream);
 
-/* Dispatch backward (un-permute and sum, router dx fused):
+/* Dispatch backward (tutorial: 专家并行与数据并行的结合 三.3: the input
+ * gradients computed on the experts' devices return to each token's device
+ * and sequence order, reversing 专家并行 二 step 2; 三.4: the router's own
+ * gradient path).  Un-permute and sum, with the router's dx fused:
  *   dx[t] = sum over kept j of dx_perm[row_of[t*k+j]]
  *           + sum_e dlogits[t, e] * w_router[:, e]
- *           (+ dx_add[t] if dx_add != NULL, e.g. the shared experts' dx). */
+ *           (+ dx_add[t] if dx_add != NULL, e.g. the shared experts' dx),
+ *   fp32 accumulation, stored in dtype.  A token with every choice dropped
+ *   gets only the router (and dx_add) terms.
+ * Errors: MOE_ERR_INVALID for a null required pointer or a misaligned
+ * dx_perm / dx / dx_add. */
 int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm,
                      const int32_t* row_of, const float* dlogits,
                      const void* w_router, const void* dx_add, void* dx,

@@ -167,10 +167,12 @@ struct KLoad {
 };
 
 // MN-contiguous source (element (k, c) at k * ld + c elements from the base
-// of the resource of the half holding column c).  2R blocks of 4 K-rows x 16
-// bytes, numbered half-major so that every wave's load reads one half: the
-// two halves of the tile's columns may come from different tensors (the
-// paired gate / up weights of SwiGLU).
+// of the half holding column c).  2R blocks of 4 K-rows x 16 bytes, numbered
+// half-major so that every wave's load reads one half: the two halves of the
+// tile's columns may come from different tensors (the paired gate / up
+// weights of SwiGLU).  Each stage reads through resources rebased at its
+// first K row (stage_res), so offsets stay within one stage whatever the
+// operand's row count.
 template <typename T, int R, int NTH>
 struct MNLoad {
   static constexpr int V = Vec16<T>::N;
@@ -198,16 +200,21 @@ struct MNLoad {
       voff[i] = (uint32_t)(((int64_t)kq4[i] * ld + c) * (int64_t)sizeof(T));
     }
   }
-  __device__ __forceinline__ void load(const BufRes& b0, const BufRes& b1, int64_t ld, int k0, int64_t Kvalid) {
+  // base0 / base1: element (0, 0) of each half's columns (the tile's first
+  // column, col0_bytes into every row); K rows [k0, k0 + BKE) of the stage.
+  __device__ __forceinline__ void load(const char* base0, const char* base1, int64_t ld, int k0, int64_t Kvalid,
+                                       int64_t col0_bytes) {
+    constexpr int BKE = ROWB / sizeof(T);
     const int row_bytes = (int)(ld * (int64_t)sizeof(T));
-    const int soff = k0 * row_bytes;
+    const BufRes b0 = stage_res(base0, k0, BKE, Kvalid, row_bytes, col0_bytes);
+    const BufRes b1 = stage_res(base1, k0, BKE, Kvalid, row_bytes, col0_bytes);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const BufRes& br = half[i] ? b1 : b0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bool ok = colok[i] && (k0 + kq4[i] + kk < Kvalid);
-        r[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(br.r, ok ? voff[i] + kk * row_bytes : kOOB, soff, 0);
+        r[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(br.r, ok ? voff[i] + kk * row_bytes : kOOB, 0, 0);
       }
     }
   }
@@ -283,14 +290,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_rows_kernel(Args a) {
   const char* Bg = reinterpret_cast<const char*>(a.B) + (int64_t)wi * a.b_gstride * S;
   const char* B2g = a.B2 ? reinterpret_cast<const char*>(a.B2) + (int64_t)wi * a.b_gstride * S : Bg;
 
+  // A: the tile's rows (at most BM); DGRAD B: the tile's BN weight rows
+  // (K-contiguous); FWD B (N-contiguous) is read stage by stage from
+  // resources rebased at each stage's first K row.
   BufRes ra, rb0, rb1;
   ra.init(Ab + row_begin * a.lda * S, rows_valid * a.lda * S);
-  if (KIND == KIND_FWD) {
-    rb0.init(Bg + n0 * S, K * a.ldb * S - n0 * S);
-    rb1.init(B2g + n0 * S, K * a.ldb * S - n0 * S);
-  } else {
-    rb0.init(Bg + n0 * a.ldb * S, (N - n0) * a.ldb * S);
-    rb1.init(B2g + n0 * a.ldb * S, (N - n0) * a.ldb * S);
+  if (KIND == KIND_DGRAD) {
+    const int64_t nrows = min((int64_t)BN, N - n0);
+    rb0.init(Bg + n0 * a.ldb * S, nrows * a.ldb * S);
+    rb1.init(B2g + n0 * a.ldb * S, nrows * a.ldb * S);
   }
   const int col_base1 = PAIR ? 0 : BN / 2;
   const int64_t valid_cols = N - n0;
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_rows_kernel(Args a) {
   auto load_stage = [&](auto& la, auto& lbk, auto& lbn, int k0) {
     la.load(ra, k0, K);
     if (KIND == KIND_FWD)
-      lbn.load(rb0, rb1, a.ldb, k0, K);
+      lbn.load(Bg + n0 * S, B2g + n0 * S, a.ldb, k0, K, n0 * S);
     else if (a.b_split > 0)
       lbk.load_split(rb0, rb1, a.ldb, k0, K, a.b_split);
     else
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_wgrad_kernel(Args a) {
   const int g = lin / per_g;
   if (g >= a.groups) return;
   int mt, nt;
-  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt);
+  grouped_order(lin - g * per_g, a.tiles_m, a.tiles_n, mt, nt, GM);
   const int wi = weight_index(g, a.rr_R, a.rr_L);
   const int64_t r0 = a.offsets[g], r1 = a.offsets[g + 1];
   const int64_t Kr = r1 - r0;
@@ -384,9 +392,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_wgrad_kernel(Args a) {
 
   const char* X = reinterpret_cast<const char*>(a.A);
   const char* D = reinterpret_cast<const char*>(a.B);
-  BufRes ra, rb;
-  ra.init(X + (r0 * a.lda + m0) * S, Kr * a.lda * S - m0 * S);
-  rb.init(D + (r0 * a.ldb + n0) * S, Kr * a.ldb * S - n0 * S);
+  const char* Xs = X + (r0 * a.lda + m0) * S;
+  const char* Ds = D + (r0 * a.ldb + n0) * S;
   MNLoad<T, BM, NTH> la0, la1;
   MNLoad<T, BN, NTH> lb0, lb1;
   la0.init(a.lda, BM / 2, M - m0);
@@ -409,8 +416,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_wgrad_kernel(Args a) {
 
   const int nk = (int)((Kr + BKE - 1) / BKE);
   auto load_stage = [&](auto& la, auto& lb, int k0) {
-    la.load(ra, ra, a.lda, k0, Kr);
-    lb.load(rb, rb, a.ldb, k0, Kr);
+    la.load(Xs, Xs, a.lda, k0, Kr, m0 * S);
+    lb.load(Ds, Ds, a.ldb, k0, Kr, n0 * S);
   };
   auto step = [&](auto& la, auto& lb, int kt) {
     char* sa = smem + (kt & 1) * (BM + BN) * ROWB;

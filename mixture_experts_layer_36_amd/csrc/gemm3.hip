@@ -119,28 +119,21 @@ __device__ __forceinline__ void lds_load16(const BufRes& b, char* lds_unit, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_unit, 16, voff, soff, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Layout of one stage of an operand in LDS.
-//   K-contiguous (KC): [R rows][BK], row pitch BK*2 bytes, 16-byte chunk c of
-//     row r stored at chunk c ^ kc_swz(r).
-//   MN-contiguous: panels of 128 columns, each [BK][128], pitch 256 bytes,
-//     chunk c of K-row k stored at chunk c ^ (4 * (k & 3)).
-// ---------------------------------------------------------------------------
-template <int BK>
-__device__ __forceinline__ int kc_swz(int row) {
-  if constexpr (BK == 32) return (row >> 2) & 3;
-  else return (row ^ (row >> 3)) & 7;
-}
-__device__ __forceinline__ int mn_swz(int k) { return 4 * (k & 3); }
+// Layout of one stage of an operand in LDS and the lanes' loads into it:
+// gemm_addr.h (kc_swz, mn_swz, kc_lane, mn_lane, shared with the host-side
+// address checker).
+using gemm_addr::kc_lane;
+using gemm_addr::kc_swz;
+using gemm_addr::mn_lane;
+using gemm_addr::mn_swz;
 
 // One operand's direct loads.  The stage is split into 1 KiB units; unit u of
 // the stage is issued by wave u % NW as its (u / NW)-th load.
 template <int R, int BK, bool KC, int NW, int W0 = 0>
 struct Loader {
-  static constexpr int BYTES = R * BK * 2;
-  static constexpr int UNITS = BYTES / 1024;
-  static_assert(UNITS % NW == 0, "units must split evenly over the waves");
-  static constexpr int PER = UNITS / NW;
+  static constexpr int BYTES = gemm_addr::Units<R, BK, NW>::BYTES;
+  static constexpr int UNITS = gemm_addr::Units<R, BK, NW>::UNITS;
+  static constexpr int PER = gemm_addr::Units<R, BK, NW>::PER;
   uint32_t voff[PER];
   int krow[PER];      // MN: K row (within the stage) this lane loads
   bool colok[PER];    // MN: column in range
@@ -148,40 +141,35 @@ struct Loader {
 
   // KC: source row r of the operand is at r * ld elements from the base.
   __device__ __forceinline__ void init_kc(int64_t ld) {
-    constexpr int CPR = BK * 2 / 16;     // chunks per row
-    constexpr int RPU = 64 / CPR;        // rows per unit
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
-    const int p = lane % CPR;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int u = i * NW + wave;
-      const int row = u * RPU + lane / CPR;
-      const int c = p ^ kc_swz<BK>(row);
-      kcol[i] = c * 8;
-      voff[i] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+      int row, col;
+      kc_lane<BK, NW>(i, wave, lane, row, col);
+      kcol[i] = col;
+      voff[i] = (uint32_t)(((int64_t)row * ld + col) * 2);
       krow[i] = 0;
       colok[i] = true;
     }
   }
-  // MN: element (k, col) at k * ld + col elements from the base of the
-  // resource of the column's panel (col relative to that base).
+  // MN: element (k0 + k, col) of a stage at k * ld + col elements from the
+  // base of the stage's resource of the column's panel (col relative to that
+  // base, k within the stage).
   __device__ __forceinline__ void init_mn(int64_t ld, bool pair, int64_t valid_cols) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
-    constexpr int KB = BK / 4;  // units per panel (4 K rows each)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int u = i * NW + wave;
-      const int panel = u / KB;
-      const int k = (u % KB) * 4 + lane / 16;
-      const int c = (lane % 16) ^ mn_swz(k);
-      const int col = (pair ? 0 : panel * 128) + c * 8;
+      int panel, k, col;
+      mn_lane<BK, NW>(i, wave, lane, pair, panel, k, col);
       krow[i] = k;
       colok[i] = col < valid_cols;
       voff[i] = (uint32_t)(((int64_t)k * ld + col) * 2);
     }
   }
-  // Issue load i (0 <= i < PER) of a stage.  KC: K range [k0, Klim);
-  // MN: K rows [k0, Klim).
+  // Issue load i (0 <= i < PER) of a stage.  KC: K range [k0, Klim), the
+  // stage's K position in the scalar offset; MN: K rows [k0, Klim), from a
+  // resource rebased at this stage's first K row (stage_res), so the scalar
+  // offset is 0 and every offset stays within one stage.
   template <typename ResOf>
   __device__ __forceinline__ void issue_one(int i, char* stage, const ResOf& res_of_panel, int k0, int64_t Klim,
                                             int64_t ld) const {
@@ -195,7 +183,7 @@ struct Loader {
       constexpr int KB = BK / 4;
       const int panel = u / KB;
       const bool ok = colok[i] && (k0 + krow[i] < Klim);
-      lds_load16(res_of_panel(panel), dst, ok ? voff[i] : kOOB, (uint32_t)((int64_t)k0 * ld * 2));
+      lds_load16(res_of_panel(panel), dst, ok ? voff[i] : kOOB, 0u);
     }
   }
 };
@@ -597,14 +585,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   const char* Bg = reinterpret_cast<const char*>(a.B) + (int64_t)wi * a.b_gstride * 2;
   const char* B2g = a.B2 ? reinterpret_cast<const char*>(a.B2) + (int64_t)wi * a.b_gstride * 2 : Bg;
 
+  // A: the tile's rows (at most BM); DGRAD B: the tile's BN weight rows
+  // (K-contiguous); FWD B (N-contiguous): rebased at every K stage in issue.
   BufRes ra, rb0, rb1;
-  ra.init(Ab + row_begin * a.lda * 2, rows_valid * a.lda * 2);
-  if (KIND == gemm::KIND_FWD) {
-    rb0.init(Bg + n0 * 2, K * a.ldb * 2 - n0 * 2);
-    rb1.init(B2g + n0 * 2, K * a.ldb * 2 - n0 * 2);
-  } else {
-    rb0.init(Bg + n0 * a.ldb * 2, (N - n0) * a.ldb * 2);
-    rb1.init(B2g + n0 * a.ldb * 2, (N - n0) * a.ldb * 2);
+  ra.init(Ab, gemm_addr::rows_a_span(row_begin, rows_valid, a.lda));
+  if (KIND == gemm::KIND_DGRAD) {
+    rb0.init(Bg, gemm_addr::dgrad_b_span(0, n0, BN, N, a.ldb));
+    rb1.init(B2g, gemm_addr::dgrad_b_span(0, n0, BN, N, a.ldb));
   }
 
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -616,8 +603,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   const bool split = BKC && a.b_split > 0;
 
   constexpr int QA = Loader<BM, BK, true, NW, W0>::PER, QB = Loader<BN, BK, BKC, NW, W0>::PER;
+  // FWD: the weights' K stages (gate and up for the pair), walked in order:
+  // every wave issues its share of each stage once, for kt = 0, 1, ...
+  StageRes w0, w1;
+  if constexpr (!BKC) {
+    w0.init(Bg, gemm_addr::fwd_b_walk(n0, BK, a.ldb));
+    w1.init(B2g, gemm_addr::fwd_b_walk(n0, BK, a.ldb));
+  }
   auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
+    BufRes s0, s1;  // FWD: this stage's K rows of the weights (gate / up for the pair)
+    if constexpr (!BKC) {
+      s0 = w0.next();
+      if (PAIR) s1 = w1.next();
+      else s1 = s0;
+    }
 #pragma unroll
     for (int q = 0; q < QA; ++q)
       if (q >= q0 && q < q1) la.issue_one(q, stage, [&](int) -> const BufRes& { return ra; }, k0, K, a.lda);
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
           lb.issue_one(q, stage + A_BYTES, [&](int) -> const BufRes& { return rb0; }, k0, split ? a.b_split : K,
                        a.ldb);
       } else {
-        lb.issue_one(q, stage + A_BYTES, [&](int p) -> const BufRes& { return (PAIR && p) ? rb1 : rb0; }, k0, K,
+        lb.issue_one(q, stage + A_BYTES, [&](int p) -> const BufRes& { return (PAIR && p) ? s1 : s0; }, k0, K,
                      a.ldb);
       }
     }
@@ -771,10 +771,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
     // split s takes rows [r0 + s*chunk, r0 + (s+1)*chunk) of the group, chunk
     // a multiple of BK; a split past the group's rows keeps an empty range
     // and writes zeros
-    const int64_t chunk = ((r1 - r0 + a.ksplit - 1) / a.ksplit + BK - 1) / BK * BK;
-    const int64_t b = r0 + split * chunk;
-    r0 = b < r1 ? b : r1;
-    r1 = b + chunk < r1 ? b + chunk : r1;
+    const int64_t g0 = r0, g1 = r1;
+    gemm_addr::split_rows(g0, g1, a.ksplit, split, BK, r0, r1);
   }
   const int64_t Kr = r1 - r0;
   const int64_t M = a.M, N = a.N;
@@ -782,17 +780,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_wgrad_kernel(Args a) {
 
   const char* X = reinterpret_cast<const char*>(a.A);
   const char* D = reinterpret_cast<const char*>(a.B);
-  BufRes ra, rb;
-  ra.init(X + (r0 * a.lda + m0) * 2, Kr * a.lda * 2 - m0 * 2);
-  rb.init(D + (r0 * a.ldb + n0) * 2, Kr * a.ldb * 2 - n0 * 2);
+  // both operands are M/N-contiguous: their resources are rebased at every
+  // K stage (rows r0 + k0 ..), so a group of any length keeps 32-bit offsets
+
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Loader<BM, BK, false, NW, W0> la;
   Loader<BN, BK, false, NW, W0> lb;
   la.init_mn(a.lda, false, M - m0);
   lb.init_mn(a.ldb, false, N - n0);
   constexpr int QA = Loader<BM, BK, false, NW, W0>::PER, QB = Loader<BN, BK, false, NW, W0>::PER;
+  // both operands' K stages, walked in order: every wave issues its share of
+  // each stage once, for kt = 0, 1, ...
+  StageRes wa, wb;
+  wa.init(X, gemm_addr::wgrad_walk(r0, m0, BK, a.lda));
+  wb.init(D, gemm_addr::wgrad_walk(r0, n0, BK, a.ldb));
   auto issue = [&](char* stage, int kt, int q0, int q1) {
     const int k0 = kt * BK;
+    const BufRes ra = wa.next(), rb = wb.next();
 #pragma unroll
     for (int q = 0; q < QA; ++q)
       if (q >= q0 && q < q1) la.issue_one(q, stage, [&](int) -> const BufRes& { return ra; }, k0, Kr, a.lda);
@@ -869,9 +873,7 @@ __global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(Args a, int epi
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
 hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
-  const int tiles_n_cols = EPI == gemm::EPI_SWIGLU_FWD ? BN / 2 : BN;
-  a.tiles_n = (int)((a.N + tiles_n_cols - 1) / tiles_n_cols);
-  a.tiles_m = (int)((rows_max + BM - 1) / BM) + a.groups;
+  gemm_addr::rows_tiles(a.N, EPI == gemm::EPI_SWIGLU_FWD ? BN / 2 : BN, rows_max, a.groups, BM, a.tiles_m, a.tiles_n);
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -885,8 +887,7 @@ hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
 
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int EPI>
 hipError_t launch_wgrad(Args a, hipStream_t st) {
-  a.tiles_m = (int)((a.M + BM - 1) / BM);
-  a.tiles_n = (int)((a.N + BN - 1) / BN);
+  gemm_addr::wgrad_tiles(a.M, a.N, BM, BN, a.tiles_m, a.tiles_n);
   const int64_t grid = (int64_t)a.groups * a.tiles_m * a.tiles_n * (EPI == kEpiPartial ? a.ksplit : 1);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -928,13 +929,7 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
 }
 
 int wgrad_ksplit(int64_t groups, int64_t M, int64_t N, int64_t rows_max) {
-  const int64_t tiles = groups * ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles <= 0 || tiles >= 512) return 1;
-  int64_t s = 512 / tiles;
-  const int64_t by_rows = rows_max / (groups > 0 ? groups : 1) / 1024;  // >= 1024 rows per split
-  if (s > by_rows) s = by_rows;
-  if (s > 8) s = 8;
-  return s < 1 ? 1 : (int)s;
+  return gemm_addr::wgrad_ksplit(groups, M, N, rows_max);
 }
 
 hipError_t run_wgrad_bf16(int epi, const Args& a, hipStream_t st) {

@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "gemm_addr.h"
 
 namespace moe {
 namespace gemm_common {
@@ -13,91 +14,82 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GM = 8;                      // row-tiles per ordering group
-constexpr uint32_t kOOB = 0x7FFFFFF0u;     // an offset beyond every extent
-constexpr int64_t kMaxExtent = 0x7FFF0000; // extents stay below kOOB
 constexpr int kRsrcWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 family
 
+// Tile order, load offsets and resource spans: gemm_addr.h (shared with the
+// host-side address checker).
+using gemm_addr::grouped_order;
+using gemm_addr::kMaxExtent;
+using gemm_addr::kMaxRowBytes;
+using gemm_addr::kOOB;
+using gemm_addr::run_remap;
+using gemm_addr::Span;
+using gemm_addr::weight_index;
+using gemm_addr::xcd_remap;
+
 // A buffer resource over [base, base + bytes): loads at offsets at or past
-// the extent return zeros (hardware range check).
+// the extent return zeros (hardware range check).  Every resource the GEMM
+// kernels build spans at most 256 rows of one operand (a row tile, a tile of
+// K-contiguous weights) or one K stage of an M/N-contiguous operand (rebased
+// at every stage, stage_res below), so its extent is bounded by the row width
+// alone; the host rejects rows wider than kMaxRowBytes, which keeps every
+// extent below kMaxExtent whatever the number of rows.  The clamp is a last
+// guard only.
 struct BufRes {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ void init(const void* base, int64_t bytes) {
     const int64_t n = bytes <= 0 ? 0 : (bytes > kMaxExtent ? kMaxExtent : bytes);
     r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
   }
+  // the span's bytes of the operand at ptr
+  __device__ __forceinline__ void init(const void* ptr, const Span& s) {
+    init(reinterpret_cast<const char*>(ptr) + s.base, s.bytes);
+  }
   __device__ __forceinline__ u32x4 ld(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   }
 };
 
-// Workgroup id -> linear tile id such that each XCD's workgroups (dispatched
-// round-robin over the 8 XCDs) get consecutive tile ids (bijection).
-__device__ __forceinline__ int xcd_remap(int hw, int num) {
-  const int q = num >> 3, r = num & 7;
-  const int xcd = hw & 7, local = hw >> 3;
-  const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-  return base + local;
+// Resource over K rows [k0, min(k0 + rows, K)) of an operand whose K row k
+// starts k * ld_bytes after `first` (which already points at the tile's first
+// column, col0_bytes into each row): loads at byte (k - k0) * ld_bytes + c
+// read row k, and rows at or past K (or past the stage) read zeros.  Built at
+// every K stage (register-staged kernels of gemm.hip), so offsets stay within
+// one stage however many rows the operand holds.
+__device__ __forceinline__ BufRes stage_res(const char* first, int64_t k0, int64_t rows, int64_t K, int64_t ld_bytes,
+                                            int64_t col0_bytes) {
+  BufRes b;
+  b.init(first + k0 * ld_bytes, (K - k0 < rows ? K - k0 : rows) * ld_bytes - col0_bytes);
+  return b;
 }
 
-// Workgroup id -> linear item id, spreading runs of C consecutive items over
-// the XCDs: item run j (items jC .. jC + C - 1) goes whole to XCD j % 8, and
-// each XCD takes its runs in order, so the items of a run keep sharing that
-// XCD's L2 while consecutive runs (the parts of one group) go to different
-// XCDs.  Items past the last whole round of 8 runs fall back to xcd_remap.
-// A bijection on [0, n).
-__device__ __forceinline__ int run_remap(int hw, int n, int C) {
-  const int span = 8 * C;
-  const int n0 = n / span * span;
-  if (hw >= n0) return n0 + xcd_remap(hw - n0, n - n0);
-  const int x = hw & 7, l = hw >> 3;
-  const int rho = l / C, off = l - rho * C;
-  return (rho * 8 + x) * C + off;
-}
+// The stages of an M/N-contiguous operand of the direct-to-LDS kernels,
+// walked in order: each call of next() gives the resource of the next stage
+// (gemm_addr::stage_span of stage 0, 1, ...), advancing the base by one
+// stride, with the extent clamped once.
+struct StageRes {
+  const char* base;
+  int64_t stride;
+  int bytes;
+  __device__ __forceinline__ void init(const void* ptr, const gemm_addr::StageWalk& w) {
+    base = reinterpret_cast<const char*>(ptr) + w.first;
+    stride = w.stride;
+    bytes = (int)(w.bytes <= 0 ? 0 : (w.bytes > kMaxExtent ? kMaxExtent : w.bytes));
+  }
+  __device__ __forceinline__ BufRes next() {
+    BufRes b;
+    b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kRsrcWord3);
+    base += stride;
+    return b;
+  }
+};
 
-// Linear tile id -> (row tile, column tile), walking GM row tiles per column
-// so that concurrently running tiles share panels in L2.
-__device__ __forceinline__ void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt, int gm = GM) {
-  const int span = gm * tiles_n;
-  const int gid = lin / span;
-  const int first = gid * gm;
-  const int gsz = min(tiles_m - first, gm);
-  const int rem = lin - gid * span;
-  mt = first + rem % gsz;
-  nt = rem / gsz;
-}
-
-// Row-split launches size the grid for the largest possible row count, since
-// the per-group row counts live on the device.  Each workgroup first counts the
-// row tiles the groups really hold; surplus workgroups exit, and the XCD remap
-// and the grouped order run over the real tiles only, so the work spreads over
-// every XCD whatever the row count.  Returns false for a surplus workgroup.
+// Device side of gemm_addr::row_tile_of over the launch's group table.
 template <int BM>
 __device__ __forceinline__ bool row_tile_of(const gemm::Args& a, int& g, int64_t& row_begin, int64_t& row_end,
                                             int& nt) {
-  int real_m = 0;
-  for (int gg = 0; gg < a.groups; ++gg) real_m += (int)((a.offsets[gg + 1] - a.offsets[gg] + BM - 1) / BM);
-  const int real = real_m * a.tiles_n;
-  if ((int)blockIdx.x >= real) return false;
-  int mt;
-  grouped_order(xcd_remap(blockIdx.x, real), real_m, a.tiles_n, mt, nt, a.gm);
-  int acc_t = 0;
-  for (int gg = 0; gg < a.groups; ++gg) {
-    const int64_t o0 = a.offsets[gg], o1 = a.offsets[gg + 1];
-    const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
-    if (mt < acc_t + nt_g) {
-      g = gg;
-      row_begin = o0 + (int64_t)(mt - acc_t) * BM;
-      row_end = o1;
-      return true;
-    }
-    acc_t += nt_g;
-  }
-  return false;
-}
-
-__device__ __forceinline__ int weight_index(int g, int rr_R, int rr_L) {
-  // send slot g = q * L + l holds expert q + R * l under round-robin placement
-  return rr_R > 0 ? (g % rr_L) * rr_R + g / rr_L : g;
+  return gemm_addr::row_tile_of<BM>(a.offsets, a.groups, a.tiles_n, a.gm, (int)blockIdx.x, g, row_begin, row_end,
+                                    nt);
 }
 
 __device__ __forceinline__ float gelu_f(float z) {

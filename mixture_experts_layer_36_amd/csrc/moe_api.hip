@@ -6,6 +6,7 @@
 #include "../../include/moe.h"
 #include "common.h"
 #include "gemm.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -40,6 +41,16 @@ int check_config(const moe_config* c) {
   if (c->n_shared > 0 && (c->n_shared * c->ffn_shared) % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->T * c->k >= (int64_t)1 << 31 || c->T >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (c->d >= (int64_t)1 << 24 || c->ffn >= (int64_t)1 << 24) return MOE_ERR_UNSUPPORTED;
+  // every buffer resource of the expert GEMMs spans at most 256 rows of one
+  // operand, so one row (x: d elements; [A | B]: 2 ffn; the shared experts:
+  // 2 n_shared ffn_shared) must stay within kMaxRowBytes for its extent to fit
+  const int64_t s = c->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  const int64_t lim = moe::gemm_common::kMaxRowBytes;
+  if (c->d * s > lim || m * c->ffn * s > lim) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 0 && (c->n_shared >= (int64_t)1 << 24 || c->ffn_shared >= (int64_t)1 << 24 ||
+                          m * c->n_shared * c->ffn_shared * s > lim))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -104,6 +115,9 @@ int check_groups(const moe_config* c, const moe_groups* g) {
   if (g->groups > 65) return MOE_ERR_UNSUPPORTED;
   if (g->ffn % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (g->rows_max >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (g->ffn >= (int64_t)1 << 24 || m * g->ffn * (int64_t)elem_bytes(c) > moe::gemm_common::kMaxRowBytes)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -232,18 +246,15 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
   return hip_status(moe::launch_route(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
 }
 
-int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm, int32_t* row_of,
-                 int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts, int64_t* expert_offsets,
-                 int32_t* send_counts, int64_t* send_offsets, void* ws, void* stream) {
-  int s = check_config(cfg);
-  if (s != MOE_OK) return s;
-  if (!x || !topk_idx || !x_perm || !row_of || !assign_of_row || !raw_counts || !expert_counts || !expert_offsets ||
-      !send_counts || !send_offsets || !ws)
-    return MOE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(x_perm) || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID;
-  const int64_t nb = (cfg->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
-  char* w = (char*)ws;
-  const size_t cnt_bytes = round_up((size_t)nb * cfg->E * 4, 256);
+}  // extern "C"
+
+namespace {
+
+// moe_dispatch with its scratch at `w`: block counts [nb, E] int32 at w, block
+// bases [nb, E] at w + cnt_bytes, expert starts [E] int64 at w + 2 cnt_bytes.
+int dispatch_into(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm, int32_t* row_of,
+                  int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts, int64_t* expert_offsets,
+                  int32_t* send_counts, int64_t* send_offsets, char* w, size_t cnt_bytes, void* stream) {
   moe::DispatchArgs a;
   a.x = x; a.topk_idx = topk_idx; a.x_perm = x_perm; a.row_of = row_of; a.assign_of_row = assign_of_row;
   a.raw_counts = raw_counts; a.expert_counts = expert_counts; a.expert_offsets = expert_offsets;
@@ -254,6 +265,34 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, 
   a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k; a.C = capacity_of(cfg);
   a.R = cfg->ep_ranks; a.placement = cfg->placement;
   return hip_status(moe::launch_dispatch(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int check_dispatch_args(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm,
+                        int32_t* row_of, int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts,
+                        int64_t* expert_offsets, int32_t* send_counts, int64_t* send_offsets) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!x || !topk_idx || !x_perm || !row_of || !assign_of_row || !raw_counts || !expert_counts || !expert_offsets ||
+      !send_counts || !send_offsets)
+    return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm, int32_t* row_of,
+                 int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts, int64_t* expert_offsets,
+                 int32_t* send_counts, int64_t* send_offsets, void* ws, void* stream) {
+  int s = check_dispatch_args(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts,
+                              expert_offsets, send_counts, send_offsets);
+  if (s != MOE_OK) return s;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID;
+  const int64_t nb = (cfg->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
+  return dispatch_into(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts, expert_offsets,
+                       send_counts, send_offsets, (char*)ws, round_up((size_t)nb * cfg->E * 4, 256), stream);
 }
 
 int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* w_in,

@@ -175,3 +175,50 @@ def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-1) == b"invalid argument"
     assert lib.moe_last_hip_error() == 0
+
+
+# The widest operand row a GEMM buffer resource of 256 rows may hold: the
+# extent cap 0x7FFF0000 bytes over 256 rows.
+MAX_ROW_BYTES = 0x7FFF0000 // 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    # d * s at the limit is accepted, one 8-element step wider is not
+    (dict(d=MAX_ROW_BYTES // 2 // 8 * 8, dtype="bf16"), nat.MOE_OK),
+    (dict(d=(MAX_ROW_BYTES // 2 // 8 + 1) * 8, dtype="bf16"), nat.MOE_ERR_UNSUPPORTED),
+    (dict(d=(MAX_ROW_BYTES // 4 // 8 + 1) * 8, dtype="f32"), nat.MOE_ERR_UNSUPPORTED),
+    # SwiGLU's [A | B] rows hold 2 ffn elements
+    (dict(ffn=MAX_ROW_BYTES // 4 // 8 * 8, act="swiglu"), nat.MOE_OK),
+    (dict(ffn=(MAX_ROW_BYTES // 4 // 8 + 1) * 8, act="swiglu"), nat.MOE_ERR_UNSUPPORTED),
+    (dict(ffn=(MAX_ROW_BYTES // 4 // 8 + 1) * 8, act="gelu"), nat.MOE_OK),
+    (dict(n_shared=2, ffn_shared=(MAX_ROW_BYTES // 8 // 8 + 1) * 8, act="swiglu"), nat.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=2, ffn_shared=MAX_ROW_BYTES // 8 // 8 * 8, act="swiglu"), nat.MOE_OK),
+])
+def test_plan_rejects_rows_wider_than_one_buffer_resource(lib, kw, status):
+    """Every buffer resource of the expert GEMMs spans at most 256 rows of an
+    operand (or one K stage of an M/N-contiguous one, rebased every stage), so
+    the only size limit left is the width of one row; wider rows are
+    rejected on the host with MOE_ERR_UNSUPPORTED."""
+    assert status_of_plan(**kw) == status
+
+
+def test_ffn_rejects_group_rows_wider_than_one_buffer_resource(lib):
+    """A caller-built group table with a hidden width whose [A | B] rows pass
+    the limit is rejected by both FFN entry points before any launch."""
+    c = nat.make_config(64, 64, 64, 8, 2, 1.0, "softmax_topk", "swiglu", "bf16")
+    cp = ctypes.byref(c)
+    fake = ctypes.c_void_p(0x100000)
+    wide = (MAX_ROW_BYTES // 4 // 8 + 1) * 8
+    g = nat.MoeGroups(groups=1, ffn=wide, rows_max=64, offsets=fake, use_placement=0)
+    assert lib.moe_expert_ffn_fwd(cp, ctypes.byref(g), *([fake] * 7), None) == nat.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_bwd(cp, ctypes.byref(g), *([fake] * 12), None) == nat.MOE_ERR_UNSUPPORTED
+
+
+def test_plan_accepts_groups_beyond_2gib_of_operand():
+    """The weight-gradient launches used to span a group's whole reduction in
+    one buffer resource, so an expert with more than ~37k rows of the
+    Mixtral-shaped [A | B] (2 x 14336 bf16 per row) read zeros past 2 GiB.
+    Resources are now rebased at every K stage: such sizes are accepted."""
+    c = nat.make_config(40000, 4096, 14336, 1, 1, 0.0, "topk_softmax", "swiglu", "bf16")
+    s = nat.plan(c)
+    assert s.n_max == 40000 and s.n_max * 2 * 14336 * 2 > 2 ** 31
