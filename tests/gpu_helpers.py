@@ -73,10 +73,13 @@ U32 = 2.0 ** -24
 
 
 def assert_dot_close(name, got, ref, abs_terms, d, tol):
-    """Inner-product outputs (d_topk_w = <dy, y_perm row>): normwise tolerance
-    plus the rounding floor of an fp32 dot product of length d,
-    gamma_d * sum_i |dy_i * o_i| (gamma_d = d u / (1 - d u), u = 2^-24).  A
-    relative error against the value itself is ill-posed when the sum cancels."""
+    """Inner-product outputs (d_topk_w = <dy, y_perm row>) of the named tiny
+    fuzz cases only: normwise tolerance plus the rounding floor of an fp32
+    dot product of length d, gamma_d * sum_i |dy_i * o_i| (gamma_d =
+    d u / (1 - d u), u = 2^-24).  A one-token case whose only inner product
+    cancels has a max|ref| far below its terms, and a bar relative to that
+    value alone is ill-posed.  Every workload and every other case uses the
+    plain normwise bar."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
@@ -120,9 +123,11 @@ def check_routing(wl, layer, ref, n_check_xperm_bits=True, x_bits=None):
     return n
 
 
-def run_full_parity(wl, inp):
+def run_full_parity(wl, inp, dot_floor=False):
     """Run one fwd+bwd step on the GPU and compare every output with the
-    oracle, element by element."""
+    oracle, element by element.  d_topk_w is held to the plain normwise bar
+    unless dot_floor is set (named tiny fuzz cases only, see
+    assert_dot_close)."""
     layer, w, x, dy = make_layer(wl, inp)
     layer.step(x, dy, w)
     torch.cuda.synchronize()
@@ -136,8 +141,11 @@ def run_full_parity(wl, inp):
     errs["y"] = assert_close("y", host(layer.y), ref["y"], tol)
     if n > 0:
         errs["y_perm"] = assert_close("y_perm", host(layer.y_perm[:n]), ref["o_perm"], tol)
-    terms = dot_abs_terms(oracle.to_f64(inp.dy), ref["o_perm"], ref["layout"]["row_of"].reshape(wl.T, wl.k))
-    errs["d_topk_w"] = assert_dot_close("d_topk_w", host(layer.d_topk_w), ref["d_topk_w"], terms, wl.d, tol)
+    if dot_floor:
+        terms = dot_abs_terms(oracle.to_f64(inp.dy), ref["o_perm"], ref["layout"]["row_of"].reshape(wl.T, wl.k))
+        errs["d_topk_w"] = assert_dot_close("d_topk_w", host(layer.d_topk_w), ref["d_topk_w"], terms, wl.d, tol)
+    else:
+        errs["d_topk_w"] = assert_close("d_topk_w", host(layer.d_topk_w), ref["d_topk_w"], tol)
     errs["dlogits"] = assert_close("dlogits", host(layer.dlogits), ref["dlogits"], tol)
     errs["dw_router"] = assert_close("dw_router", host(layer.dw_router), ref["dw_router"], tol)
     errs["dw1"] = assert_close("dw1", host(layer.dw1), ref["dw1"], tol)
@@ -154,113 +162,6 @@ def run_full_parity(wl, inp):
     kept = ref["layout"]["kept_counts"]
     for e in np.nonzero(kept == 0)[0]:
         assert np.all(host(layer.dw1[e]) == 0.0) and np.all(host(layer.dw2[e]) == 0.0)
+        if wl.act == "swiglu":
+            assert np.all(host(layer.dw_up[e]) == 0.0)
     return layer, ref, errs
-
-
-def run_sampled_parity(wl, inp, n_tok=12, n_cols=6, seed=1):
-    """Full-size check: every integer output and the logits in full; float
-    outputs on sampled tokens (y, y_perm rows, d_topk_w, dlogits, dx) and
-    sampled hidden units of every expert's weight gradients, each computed
-    one by one by the oracle; dW_r through the identity dW_r = x^T dlogits
-    (holds at any size) with dlogits itself checked on the sample."""
-    layer, w, x, dy = make_layer(wl, inp)
-    layer.step(x, dy, w)
-    torch.cuda.synchronize()
-    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.ffn
-    tol = TOL[wl.dtype]
-    swiglu = wl.act == "swiglu"
-    X = oracle.to_f64(inp.x)
-    DY = oracle.to_f64(inp.dy)
-    Wr = oracle.to_f64(inp.w_router)
-    bias = None if inp.bias is None else oracle.to_f64(inp.bias)
-    g_logits = host(layer.logits)
-    assert_close("logits", g_logits, oracle.gate_logits(X, Wr, bias), TOL_LOGITS)
-    idx = oracle.select_topk(g_logits, k)
-    gw = oracle.gate_weights(g_logits, idx, wl.gating)
-    C = oracle.capacity(T, E, k, wl.capacity_factor)
-    lay = oracle.dispatch_layout(idx, E, C, wl.ep_ranks, wl.placement)
-    check_routing(wl, layer, dict(topk_idx=idx, layout=lay), x_bits=storage_bits(inp.x))
-    assert_close("topk_w", host(layer.topk_w), gw, 1e-5)
-
-    rng = np.random.default_rng(seed)
-    toks = sorted(set([0, T - 1] + [int(t) for t in rng.choice(T, n_tok, replace=False)]))
-    cols = sorted(set([0, F - 1] + [int(c) for c in rng.choice(F, n_cols, replace=False)]))
-    row_of = lay["row_of"].reshape(T, k)
-    ns = len(toks)
-    y_ref = np.zeros((ns, d))
-    dtw_ref = np.zeros((ns, k))
-    dtw_terms = np.zeros((ns, k))
-    dx_ref = np.zeros((ns, d))
-    yp_got, yp_ref = [], []
-    cols_t = torch.tensor(cols, device=layer.dw1.device)
-    dw_got = {"dw1": [], "dw2": [], "dw_up": []}
-    dw_ref = {"dw1": [], "dw2": [], "dw_up": []}
-    off = lay["expert_offsets"]
-    slot_of = {int(e): s for s, e in enumerate(lay["slot_expert"])}
-    g_yperm = layer.y_perm
-    for e in range(E):
-        W1 = oracle.to_f64(inp.w1[e])
-        W2 = oracle.to_f64(inp.w2[e])
-        WU = oracle.to_f64(inp.w_up[e]) if swiglu else None
-        sel = [(i, j) for i, t in enumerate(toks) for j in range(k)
-               if idx[t, j] == e and row_of[t, j] >= 0]
-        if sel:
-            xs = X[[toks[i] for i, _ in sel]]
-            o = oracle.expert_ffn_forward(xs, W1, W2, wl.act, WU)["o"]
-            do = np.stack([gw[toks[i], j] * DY[toks[i]] for i, j in sel])
-            dxp = oracle.expert_ffn_backward(xs, do, W1, W2, wl.act, WU)["dxp"]
-            for r, (i, j) in enumerate(sel):
-                t = toks[i]
-                y_ref[i] += gw[t, j] * o[r]
-                dtw_ref[i, j] = DY[t] @ o[r]
-                dtw_terms[i, j] = np.sum(np.abs(DY[t] * o[r]))
-                dx_ref[i] += dxp[r]
-                yp_got.append(host(g_yperm[int(row_of[t, j])]))
-                yp_ref.append(o[r])
-        s = slot_of[e]
-        a = lay["assign_of_row"][off[s]:off[s + 1]]
-        tk, jj = a // k, a % k
-        xp_e = X[tk]
-        do_e = gw[tk, jj][:, None] * DY[tk]
-        b = oracle.expert_ffn_backward(xp_e, do_e, W1[:, cols], W2[cols, :], wl.act,
-                                       None if WU is None else WU[:, cols])
-        dw_got["dw1"].append(host(layer.dw1[e].index_select(1, cols_t)))
-        dw_ref["dw1"].append(b["dw_in"])
-        dw_got["dw2"].append(host(layer.dw2[e].index_select(0, cols_t)))
-        dw_ref["dw2"].append(b["dw_out"])
-        if swiglu:
-            dw_got["dw_up"].append(host(layer.dw_up[e].index_select(1, cols_t)))
-            dw_ref["dw_up"].append(b["dw_up"])
-    if wl.n_shared:
-        Fs = wl.ffn_shared
-        SG, SD = oracle.to_f64(inp.ws_gate), oracle.to_f64(inp.ws_down)
-        SU = oracle.to_f64(inp.ws_up) if swiglu else None
-        scols = sorted(set([0, wl.n_shared * Fs - 1] + [int(c) for c in rng.choice(wl.n_shared * Fs, n_cols, replace=False)]))
-        for sidx in range(wl.n_shared):
-            c = slice(sidx * Fs, (sidx + 1) * Fs)
-            f = oracle.expert_ffn_forward(X[toks], SG[:, c], SD[c, :], wl.act, None if SU is None else SU[:, c])
-            y_ref += f["o"]
-            dx_ref += oracle.expert_ffn_backward(X[toks], DY[toks], SG[:, c], SD[c, :], wl.act,
-                                                 None if SU is None else SU[:, c])["dxp"]
-        bs = oracle.expert_ffn_backward(X, DY, SG[:, scols], SD[scols, :], wl.act,
-                                        None if SU is None else SU[:, scols])
-        assert_close("dws_gate[cols]", host(layer.dws_gate)[:, scols], bs["dw_in"], tol)
-        assert_close("dws_down[cols]", host(layer.dws_down)[scols, :], bs["dw_out"], tol)
-        if swiglu:
-            assert_close("dws_up[cols]", host(layer.dws_up)[:, scols], bs["dw_up"], tol)
-    dl_ref = oracle.gating_backward(g_logits[toks], idx[toks], dtw_ref, wl.gating)
-    dx_ref += dl_ref @ Wr.T
-    errs = {}
-    errs["y"] = assert_close("y[tokens]", host(layer.y)[toks], y_ref, tol)
-    errs["y_perm"] = assert_close("y_perm[rows]", np.stack(yp_got), np.stack(yp_ref), tol)
-    errs["d_topk_w"] = assert_dot_close("d_topk_w[tokens]", host(layer.d_topk_w)[toks], dtw_ref, dtw_terms, d,
-                                        tol)
-    g_dl = host(layer.dlogits)
-    errs["dlogits"] = assert_close("dlogits[tokens]", g_dl[toks], dl_ref, tol)
-    errs["dx"] = assert_close("dx[tokens]", host(layer.dx)[toks], dx_ref, tol)
-    for key in ("dw1", "dw2", "dw_up"):
-        if dw_got[key]:
-            errs[key] = assert_close(key + "[cols]", np.stack(dw_got[key]), np.stack(dw_ref[key]), tol)
-    errs["dw_router"] = assert_close("dw_router = x^T dlogits", host(layer.dw_router), X.T @ g_dl, tol)
-    np.testing.assert_allclose(g_dl.sum(axis=1), 0.0, atol=1e-4 * max(1.0, np.abs(g_dl).max()))
-    return layer, errs
