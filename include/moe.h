@@ -160,6 +160,23 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                  int64_t* expert_offsets, int32_t* send_counts,
                  int64_t* send_offsets, void* ws, void* stream);
 
+/* moe_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * moe_dispatch minus `ws`.  Its scratch (per-block expert counts and bases,
+ * the experts' first rows) is a static device array of 2 MiB + 512 bytes
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing.  Limits: cfg->T <= 2^20 tokens (MOE_ERR_UNSUPPORTED
+ * beyond).  `stream` must belong to the calling thread's current device.
+ * Calls that overlap in time on one GPU (on different streams) share that
+ * scratch and race: order them on one stream. */
+int moe_dispatch_noalloc(const moe_config* cfg, const void* x,
+                         const int32_t* topk_idx, void* x_perm,
+                         int32_t* row_of, int32_t* assign_of_row,
+                         int32_t* raw_counts, int32_t* expert_counts,
+                         int64_t* expert_offsets, int32_t* send_counts,
+                         int64_t* send_offsets, void* stream);
+
 /* Grouped expert FFN forward (tutorial: 专家并行 二 step 3, local experts;
  * 框架: ffn experts), MFMA with fp32 accumulation.
  *   x_rows [rows_max, d]; weights per expert:

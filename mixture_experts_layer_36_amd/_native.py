@@ -48,6 +48,7 @@ SIGNATURES = {
     "moe_plan": [_CFG, ctypes.POINTER(MoeSizes)],
     "moe_route": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_dispatch": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_dispatch_noalloc": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn_fwd": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn_bwd": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_combine": [_CFG, _P, _P, _P, _P, _P, _P],

@@ -47,6 +47,13 @@ def moe_dispatch(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, ex
          _ptr(send_counts), _ptr(send_offsets), _ptr(ws), _stream(stream))
 
 
+def moe_dispatch_noalloc(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts,
+                         expert_offsets, send_counts, send_offsets, stream=None):
+    call("moe_dispatch_noalloc", ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(x_perm), _ptr(row_of),
+         _ptr(assign_of_row), _ptr(raw_counts), _ptr(expert_counts), _ptr(expert_offsets),
+         _ptr(send_counts), _ptr(send_offsets), _stream(stream))
+
+
 def moe_expert_ffn_fwd(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, y_rows, stream=None):
     call("moe_expert_ffn_fwd", ctypes.byref(cfg), ctypes.byref(grp), _ptr(x_rows), _ptr(w_in),
          _ptr(w_up), _ptr(w_out), _ptr(act_saved), _ptr(h), _ptr(y_rows), _stream(stream))

@@ -9,7 +9,20 @@
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <mutex>
 #include <type_traits>
+
+// Scratch of moe_dispatch_noalloc: the dispatch kernels' per-block expert
+// counts, per-block bases (inputs of more than 128 blocks) and the experts'
+// first rows, for at most 2^20 tokens and 64 experts (2 MiB + 512 bytes).
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the name
+// is only a stand-in): it uses the device address hipGetSymbolAddress returns
+// for the current device (scratch_base below).
+constexpr int64_t kNoAllocMaxTokens = (int64_t)1 << 20;
+constexpr size_t kNoAllocCntBytes = (size_t)(kNoAllocMaxTokens / moe::kDispatchBlock) * 64 * 4;
+constexpr size_t kNoAllocBytes = 2 * kNoAllocCntBytes + 64 * 8;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
 
 namespace {
 
@@ -250,6 +263,29 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
 
 namespace {
 
+// Per-device address of `scratch`, looked up once per device (with that
+// device current) on the first moe_dispatch_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_base(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 // moe_dispatch with its scratch at `w`: block counts [nb, E] int32 at w, block
 // bases [nb, E] at w + cnt_bytes, expert starts [E] int64 at w + 2 cnt_bytes.
 int dispatch_into(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm, int32_t* row_of,
@@ -293,6 +329,22 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx, 
   const int64_t nb = (cfg->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
   return dispatch_into(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts, expert_offsets,
                        send_counts, send_offsets, (char*)ws, round_up((size_t)nb * cfg->E * 4, 256), stream);
+}
+
+int moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx, void* x_perm,
+                         int32_t* row_of, int32_t* assign_of_row, int32_t* raw_counts, int32_t* expert_counts,
+                         int64_t* expert_offsets, int32_t* send_counts, int64_t* send_offsets, void* stream) {
+  int s = check_dispatch_args(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts,
+                              expert_offsets, send_counts, send_offsets);
+  if (s != MOE_OK) return s;
+  if (cfg->T > kNoAllocMaxTokens) return MOE_ERR_UNSUPPORTED;
+  char* w = nullptr;
+  s = scratch_base(&w);
+  if (s != MOE_OK) return s;
+  // every scratch word a call reads it first writes itself (block counts for
+  // every block and expert, then the bases and starts), so nothing is cleared
+  return dispatch_into(cfg, x, topk_idx, x_perm, row_of, assign_of_row, raw_counts, expert_counts, expert_offsets,
+                       send_counts, send_offsets, w, kNoAllocCntBytes, stream);
 }
 
 int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* w_in,
