@@ -347,6 +347,41 @@ def router_backward(x, w_router, dlogits):
     return x.T @ dlogits, dlogits @ w_router.T
 
 
+# --------------------------------------------------------------------------
+# load-balancing loss  [FW: DeepSpeed's moe block takes a "loss_coef", the
+# load-balancing loss coefficient; the model config of 实践 四 an
+# "aux_loss_factor"; 实践 七.3 负载均衡: the logged auxiliary loss should be
+# close to 0 with every expert chosen about equally often]
+# --------------------------------------------------------------------------
+def balance_loss(logits, idx, E: int, coef: float) -> float:
+    """Auxiliary balance loss.  The pages give its coefficient and its goal,
+    not its formula; the reading adopted is the usual product of the two
+    per-expert loads:
+
+        L = coef * E * sum_e f_e * P_e
+
+    f_e: the share of the T*k routing choices that picked expert e (before
+    capacity, so drops do not hide an overloaded expert);
+    P_e: the mean over tokens of softmax(l_t)[e], bias included.
+    With every expert chosen equally often (f_e = 1/E) L = coef, small for the
+    pages' coefficients (0.01 - 0.1); when the choices pile onto the experts
+    the router favours, L grows towards coef * E / k."""
+    T, k = idx.shape
+    f = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64) / (T * k)
+    P = softmax(np.asarray(logits, dtype=np.float64), axis=1).mean(axis=0)
+    return float(coef * E * np.sum(f * P))
+
+
+def balance_loss_grad(logits, idx, E: int, coef: float) -> np.ndarray:
+    """dL/dl[t, j] of balance_loss: f is piecewise constant in the logits, so
+    only P_e moves, and through the softmax Jacobian
+        dL/dl[t, j] = coef * E / T * p[t, j] * (f_j - sum_e f_e p[t, e])."""
+    T, k = idx.shape
+    f = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64) / (T * k)
+    p = softmax(np.asarray(logits, dtype=np.float64), axis=1)
+    return coef * E / T * p * (f[None, :] - (p @ f)[:, None])
+
+
 def unpermute_sum(dxp, row_of) -> np.ndarray:
     """dx[t] = sum over kept j of dxp[row(t, j)] (sequence order restored,
     [EP] 二 step 4)."""
@@ -371,7 +406,7 @@ def layer_forward_backward(x, w_router, bias, w1, w_up, w2, dy, *, k: int,
                            ep_ranks: int = 1, placement: str = "contiguous",
                            ws_gate=None, ws_up=None, ws_down=None,
                            n_shared: int = 0, logits=None,
-                           backward: bool = True) -> dict:
+                           backward: bool = True, aux_coef: float = 0.0) -> dict:
     """Forward and backward of the layer on float64 inputs.
 
     x [T, d], w_router [d, E], bias [E] or None, w1 / w_up [E, d, F],
@@ -380,6 +415,8 @@ def layer_forward_backward(x, w_router, bias, w1, w_up, w2, dy, *, k: int,
     If ``logits`` is given (e.g. the fp32 logits another implementation
     produced), routing decisions are taken on those values; the layer's own
     gate product is still returned as ``logits_ref``.
+    With aux_coef != 0 the balance loss (balance_loss) is returned as
+    ``aux_loss`` and the backward differentiates <dy, y> + aux_loss.
     """
     T, d = x.shape
     E = w_router.shape[1]
@@ -392,6 +429,7 @@ def layer_forward_backward(x, w_router, bias, w1, w_up, w2, dy, *, k: int,
     C = capacity(T, E, k, capacity_factor)
     lay = dispatch_layout(idx, E, C, ep_ranks, placement)
     out.update(topk_idx=idx, topk_w=g, C=C, layout=lay)
+    out["aux_loss"] = balance_loss(lg, idx, E, aux_coef) if aux_coef else 0.0
     xp = permute_rows(x, lay, k)
     out["x_perm"] = xp
     n = lay["n"]
@@ -462,6 +500,8 @@ def layer_forward_backward(x, w_router, bias, w1, w_up, w2, dy, *, k: int,
                 dwsu[:, cols] = b["dw_up"]
         out.update(dx_shared=dx_shared, dws_gate=dwsg, dws_up=dwsu, dws_down=dwsd)
     dl = gating_backward(lg, idx, dg, gating)
+    if aux_coef:
+        dl = dl + balance_loss_grad(lg, idx, E, aux_coef)
     dwr, dx_router = router_backward(x, w_router, dl)
     out.update(dlogits=dl, dw_router=dwr, dx_router=dx_router)
     dx = unpermute_sum(dxp, row_of) + dx_router
@@ -482,4 +522,5 @@ def layer_from_inputs(inp, logits=None, backward: bool = True) -> dict:
         capacity_factor=wl.capacity_factor, ep_ranks=wl.ep_ranks,
         placement=wl.placement, ws_gate=to_f64(inp.ws_gate),
         ws_up=to_f64(inp.ws_up), ws_down=to_f64(inp.ws_down),
-        n_shared=wl.n_shared, logits=logits, backward=backward)
+        n_shared=wl.n_shared, logits=logits, backward=backward,
+        aux_coef=getattr(wl, "aux_coef", 0.0))

@@ -41,6 +41,7 @@ class Workload:
     n_shared: int = 0           # always-on shared experts
     ffn_shared: int = 0         # hidden width of each shared expert
     zipf_s: float = 0.0         # > 0: router bias 2 ln Zipf(s) probabilities
+    aux_coef: float = 0.0       # != 0: balance loss coefficient (loss_coef)
     seed: int = 0x4D6F45        # base seed of the workload's tensors
     w_std: float = 0.02         # weight standard deviation
 
