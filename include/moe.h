@@ -235,12 +235,43 @@ int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* y_perm,
 /* Router backward (tutorial: 专家并行与数据并行的结合 三.4, router
  * gradients).  dlogits [T, E] fp32 through the gate-weight Jacobian:
  *   SOFTMAX_TOPK: dl = p (dp - <p, dp>), dp[e_j] = d_topk_w[t, j], else 0;
- *   RENORM / TOPK_SOFTMAX: dl[e_j] = g_j (dg_j - sum_m g_m dg_m), 0 elsewhere.
+ *   RENORM / TOPK_SOFTMAX: dl[e_j] = g_j (dg_j - sum_m g_m dg_m), 0 elsewhere;
+ *   plus dlogits_add [T, E] fp32 when not NULL: another gradient of the
+ *   logits, such as moe_aux_loss_bwd's, so that dlogits, dw_router and the
+ *   router term of moe_dispatch_bwd carry it too.
  * dw_router [d, E] dtype = x^T dlogits (deterministic two-stage reduction).
  * The bias gets no gradient.  ws: moe_plan's workspace. */
 int moe_route_bwd(const moe_config* cfg, const void* x, const float* logits,
                   const int32_t* topk_idx, const float* d_topk_w,
-                  float* dlogits, void* dw_router, void* ws, void* stream);
+                  const float* dlogits_add, float* dlogits, void* dw_router,
+                  void* ws, void* stream);
+
+/* Auxiliary load-balancing loss (tutorial: 用于分布式 MoE 的主流框架与库 一,
+ * DeepSpeed's moe block and its loss_coef, the load-balancing loss
+ * coefficient; 实践 七.3: the logged auxiliary loss should be near 0 with
+ * experts chosen about equally often).  The pages give no formula; the one
+ * computed is
+ *   loss = coef * E * sum_e f_e P_e,
+ * f_e = raw_counts[e] / (T k), the share of the routing choices on expert e
+ * (moe_dispatch's raw counts, before capacity), P_e = the mean over tokens
+ * of softmax(logits[t])[e].  Equal choice counts give loss = coef.
+ *   logits [T, E] fp32 (moe_route's), raw_counts [E] int32;
+ *   loss: DEVICE pointer to one fp32, written;
+ *   ws: moe_plan's workspace (the per-workgroup partial sums, fixed order,
+ *   so the loss is deterministic).
+ * Errors: MOE_ERR_INVALID for a null pointer, a NaN coef or a misaligned ws. */
+int moe_aux_loss(const moe_config* cfg, const float* logits,
+                 const int32_t* raw_counts, float coef, float* loss, void* ws,
+                 void* stream);
+
+/* Gradient of moe_aux_loss's loss (upstream gradient 1) with respect to the
+ * logits, f held constant (it changes only where the top-k does):
+ *   dlogits_aux[t, e] = coef * E / T * p[t, e] * (f_e - sum_m f_m p[t, m]),
+ * p = softmax(logits[t]); [T, E] fp32, written.  Pass it to moe_route_bwd as
+ * dlogits_add.  Errors: MOE_ERR_INVALID for a null pointer or a NaN coef. */
+int moe_aux_loss_bwd(const moe_config* cfg, const float* logits,
+                     const int32_t* raw_counts, float coef, float* dlogits_aux,
+                     void* stream);
 
 /* Dispatch backward (tutorial: 专家并行与数据并行的结合 三.3: the input
  * gradients computed on the experts' devices return to each token's device

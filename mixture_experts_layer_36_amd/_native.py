@@ -53,7 +53,9 @@ SIGNATURES = {
     "moe_expert_ffn_bwd": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_combine": [_CFG, _P, _P, _P, _P, _P, _P],
     "moe_combine_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P],
-    "moe_route_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_route_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_aux_loss": [_CFG, _P, _P, ctypes.c_float, _P, _P, _P],
+    "moe_aux_loss_bwd": [_CFG, _P, _P, ctypes.c_float, _P, _P],
     "moe_dispatch_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P],
     "moe_status_string": [ctypes.c_int],
     "moe_last_hip_error": [],

@@ -76,9 +76,19 @@ def moe_combine_bwd(cfg, dy, y_perm, row_of, topk_w, dy_perm, d_topk_w, stream=N
          _ptr(topk_w), _ptr(dy_perm), _ptr(d_topk_w), _stream(stream))
 
 
-def moe_route_bwd(cfg, x, logits, topk_idx, d_topk_w, dlogits, dw_router, ws, stream=None):
+def moe_route_bwd(cfg, x, logits, topk_idx, d_topk_w, dlogits_add, dlogits, dw_router, ws, stream=None):
     call("moe_route_bwd", ctypes.byref(cfg), _ptr(x), _ptr(logits), _ptr(topk_idx),
-         _ptr(d_topk_w), _ptr(dlogits), _ptr(dw_router), _ptr(ws), _stream(stream))
+         _ptr(d_topk_w), _ptr(dlogits_add), _ptr(dlogits), _ptr(dw_router), _ptr(ws), _stream(stream))
+
+
+def moe_aux_loss(cfg, logits, raw_counts, coef, loss, ws, stream=None):
+    call("moe_aux_loss", ctypes.byref(cfg), _ptr(logits), _ptr(raw_counts), ctypes.c_float(coef),
+         _ptr(loss), _ptr(ws), _stream(stream))
+
+
+def moe_aux_loss_bwd(cfg, logits, raw_counts, coef, dlogits_aux, stream=None):
+    call("moe_aux_loss_bwd", ctypes.byref(cfg), _ptr(logits), _ptr(raw_counts), ctypes.c_float(coef),
+         _ptr(dlogits_aux), _stream(stream))
 
 
 def moe_dispatch_bwd(cfg, dx_perm, row_of, dlogits, w_router, dx_add, dx, stream=None):

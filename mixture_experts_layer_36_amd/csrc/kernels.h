@@ -33,6 +33,7 @@ struct CombineArgs {
 
 struct RouteBwdArgs {
   const void* x; const float* logits; const int32_t* topk_idx; const float* d_topk_w;
+  const float* dlogits_add;  // nullable: another gradient of the logits, added to the gating Jacobian's
   float* dlogits; void* dw_router; float* partial;
   int64_t T; int64_t d; int E; int k; int gating;
 };
@@ -41,6 +42,14 @@ struct DispatchBwdArgs {
   const void* dx_perm; const int32_t* row_of; const float* dlogits; const void* w_router;
   const void* dx_add; void* dx;
   int64_t T; int64_t d; int E; int k;
+};
+
+struct AuxArgs {
+  const float* logits; const int32_t* raw_counts; float coef;
+  float* loss;       // forward: device scalar
+  float* partial;    // forward: workspace, aux_ws_bytes(E)
+  float* dlogits;    // backward: [T, E]
+  int64_t T; int E; int k;
 };
 
 hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st);
@@ -53,5 +62,10 @@ hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t 
 hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st);
 
 int router_wgrad_blocks(int64_t T);
+
+hipError_t launch_aux_loss(const AuxArgs& a, hipStream_t st);
+hipError_t launch_aux_loss_bwd(const AuxArgs& a, hipStream_t st);
+// bytes of ws the balance loss uses for its partial sums
+size_t aux_ws_bytes(int64_t E);
 
 }  // namespace moe

@@ -82,7 +82,7 @@ int64_t plan_n_max(const moe_config* c) {
 size_t elem_bytes(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
 struct WsLayout {
-  size_t dispatch, route, route_bwd, ffn_routed, ffn_shared, total;
+  size_t dispatch, route, route_bwd, aux, ffn_routed, ffn_shared, total;
 };
 
 // Workspace of one moe_expert_ffn_bwd call over `groups` groups of hidden
@@ -113,9 +113,11 @@ WsLayout ws_layout(const moe_config* c, int64_t n_max) {
   w.ffn_routed = ffn_bwd_ws(c, c->E, c->ffn, n_max);
   w.ffn_shared = c->n_shared > 0 ? ffn_bwd_ws(c, 1, c->n_shared * c->ffn_shared, c->T) : 0;
   w.route = c->dtype == MOE_BF16 ? round_up(moe::route_ws_bytes(c->d, c->E), 256) : 0;
+  w.aux = round_up(moe::aux_ws_bytes(c->E), 256);
   w.total = w.dispatch;
   if (w.route > w.total) w.total = w.route;
   if (w.route_bwd > w.total) w.total = w.route_bwd;
+  if (w.aux > w.total) w.total = w.aux;
   if (w.ffn_routed > w.total) w.total = w.ffn_routed;
   if (w.ffn_shared > w.total) w.total = w.ffn_shared;
   return w;
@@ -418,16 +420,41 @@ int moe_combine_bwd(const moe_config* cfg, const void* dy, const void* y_perm, c
 }
 
 int moe_route_bwd(const moe_config* cfg, const void* x, const float* logits, const int32_t* topk_idx,
-                  const float* d_topk_w, float* dlogits, void* dw_router, void* ws, void* stream) {
+                  const float* d_topk_w, const float* dlogits_add, float* dlogits, void* dw_router, void* ws,
+                  void* stream) {
   int s = check_config(cfg);
   if (s != MOE_OK) return s;
   if (!x || !logits || !topk_idx || !d_topk_w || !dlogits || !dw_router || !ws) return MOE_ERR_INVALID;
   if ((uintptr_t)ws & 255u) return MOE_ERR_INVALID;
   moe::RouteBwdArgs a{};
-  a.x = x; a.logits = logits; a.topk_idx = topk_idx; a.d_topk_w = d_topk_w; a.dlogits = dlogits;
+  a.x = x; a.logits = logits; a.topk_idx = topk_idx; a.d_topk_w = d_topk_w; a.dlogits_add = dlogits_add;
+  a.dlogits = dlogits;
   a.dw_router = dw_router; a.partial = (float*)ws;
   a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k; a.gating = cfg->gating;
   return hip_status(moe::launch_route_bwd(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_aux_loss(const moe_config* cfg, const float* logits, const int32_t* raw_counts, float coef, float* loss,
+                 void* ws, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!logits || !raw_counts || !loss || !ws) return MOE_ERR_INVALID;
+  if (!(coef == coef) || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID;
+  moe::AuxArgs a{};
+  a.logits = logits; a.raw_counts = raw_counts; a.coef = coef; a.loss = loss; a.partial = (float*)ws;
+  a.T = cfg->T; a.E = (int)cfg->E; a.k = (int)cfg->k;
+  return hip_status(moe::launch_aux_loss(a, (hipStream_t)stream));
+}
+
+int moe_aux_loss_bwd(const moe_config* cfg, const float* logits, const int32_t* raw_counts, float coef,
+                     float* dlogits_aux, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!logits || !raw_counts || !dlogits_aux || !(coef == coef)) return MOE_ERR_INVALID;
+  moe::AuxArgs a{};
+  a.logits = logits; a.raw_counts = raw_counts; a.coef = coef; a.dlogits = dlogits_aux;
+  a.T = cfg->T; a.E = (int)cfg->E; a.k = (int)cfg->k;
+  return hip_status(moe::launch_aux_loss_bwd(a, (hipStream_t)stream));
 }
 
 int moe_dispatch_bwd(const moe_config* cfg, const void* dx_perm, const int32_t* row_of, const float* dlogits,

@@ -19,10 +19,13 @@ namespace moe {
 // G lanes per token (G = E rounded up to a power of two, at least 8), 64 / G
 // tokens per wave; the softmax statistics and the weighted sums are
 // reductions over the token's G lanes.
+// dl_add (nullable): another gradient of the logits (the balance loss's),
+// added to the Jacobian's.
 template <int G>
 __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict__ logits,
                                                          const int32_t* __restrict__ idx,
-                                                         const float* __restrict__ dg, float* __restrict__ dl,
+                                                         const float* __restrict__ dg,
+                                                         const float* __restrict__ dl_add, float* __restrict__ dl,
                                                          int64_t Tn, int E, int k, int gating) {
   const int lane = threadIdx.x & 63;
   const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict
     const float s = group_sum<G>(g * dgl);
     out = sel >= 0 ? g * (dgl - s) : 0.0f;
   }
-  if (valid) dl[t * E + e] = out;
+  if (valid) dl[t * E + e] = dl_add ? out + dl_add[t * E + e] : out;
 }
 
 template <int G>
@@ -60,7 +63,7 @@ static hipError_t launch_gating_bwd(const RouteBwdArgs& a, hipStream_t st) {
   const int64_t blocks = (a.T + TPB - 1) / TPB;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((gating_bwd_kernel<G>), dim3((unsigned)blocks), dim3(256), 0, st, a.logits, a.topk_idx,
-                     a.d_topk_w, a.dlogits, a.T, a.E, a.k, a.gating);
+                     a.d_topk_w, a.dlogits_add, a.dlogits, a.T, a.E, a.k, a.gating);
   return hipGetLastError();
 }
 

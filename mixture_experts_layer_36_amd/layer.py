@@ -4,10 +4,14 @@
 memory, following the "pre-allocate and reuse buffers" advice of the
 tutorial's 通信优化方法 section) and issues the C entry points in order:
 
-  forward : moe_route -> moe_dispatch -> moe_expert_ffn_fwd (routed, then
-            shared experts) -> moe_combine
+  forward : moe_route -> moe_dispatch (-> moe_aux_loss) -> moe_expert_ffn_fwd
+            (routed, then shared experts) -> moe_combine
   backward: moe_combine_bwd -> moe_expert_ffn_bwd (routed, then shared)
-            -> moe_route_bwd -> moe_dispatch_bwd
+            (-> moe_aux_loss_bwd) -> moe_route_bwd -> moe_dispatch_bwd
+
+With aux_coef != 0 the step also computes the balance loss (DeepSpeed's
+loss_coef in the tutorial's framework section) and differentiates it with
+upstream gradient 1, alongside <dy, y>.
 
 All of it is enqueued on one stream with no host synchronisation.
 """
@@ -38,7 +42,7 @@ class Weights:
 
 class MoELayer:
     def __init__(self, T, d, ffn, E, k, capacity_factor, gating, act, dtype, ep_ranks=1,
-                 placement="contiguous", n_shared=0, ffn_shared=0, device="cuda"):
+                 placement="contiguous", n_shared=0, ffn_shared=0, device="cuda", aux_coef=0.0):
         self.cfg = make_config(T, d, ffn, E, k, capacity_factor, gating, act, dtype, ep_ranks,
                                placement, n_shared, ffn_shared)
         self.sizes = plan(self.cfg)
@@ -89,6 +93,10 @@ class MoELayer:
             self.dws_gate = e(d, self.Fs)
             self.dws_up = e(d, self.Fs) if act == "swiglu" else None
             self.dws_down = e(self.Fs, d)
+        self.aux_coef = float(aux_coef)
+        if self.aux_coef:
+            self.aux_loss = e(1, dtype=torch.float32)
+            self.dlogits_aux = e(T, E, dtype=torch.float32)
         self.ws = e(max(1, (self.sizes.workspace_bytes + 255) // 256 * 256), dtype=torch.uint8)
         self.grp = api.groups(E, ffn, n, self.expert_offsets, use_placement=True)
         if n_shared > 0:
@@ -129,9 +137,15 @@ class MoELayer:
                                self.s_h, dy, self.dx_shared, self.dws_gate, self.dws_up,
                                self.dws_down, self.ws)
 
+    def aux_fwd(self):
+        api.moe_aux_loss(self.cfg, self.logits, self.raw_counts, self.aux_coef, self.aux_loss, self.ws)
+
+    def aux_bwd(self):
+        api.moe_aux_loss_bwd(self.cfg, self.logits, self.raw_counts, self.aux_coef, self.dlogits_aux)
+
     def route_bwd(self, x):
-        api.moe_route_bwd(self.cfg, x, self.logits, self.topk_idx, self.d_topk_w, self.dlogits,
-                          self.dw_router, self.ws)
+        api.moe_route_bwd(self.cfg, x, self.logits, self.topk_idx, self.d_topk_w,
+                          self.dlogits_aux if self.aux_coef else None, self.dlogits, self.dw_router, self.ws)
 
     def dispatch_bwd(self, w: Weights):
         api.moe_dispatch_bwd(self.cfg, self.dx_perm, self.row_of, self.dlogits, w.w_router,
@@ -140,6 +154,8 @@ class MoELayer:
     def forward(self, x, w: Weights):
         self.route(x, w)
         self.dispatch(x)
+        if self.aux_coef:
+            self.aux_fwd()
         self.experts_fwd(w)
         if self.n_shared:
             self.shared_fwd(x, w)
@@ -151,6 +167,8 @@ class MoELayer:
         self.experts_bwd(w)
         if self.n_shared:
             self.shared_bwd(x, dy, w)
+        if self.aux_coef:
+            self.aux_bwd()
         self.route_bwd(x)
         self.dispatch_bwd(w)
         return self.dx

@@ -42,7 +42,7 @@ def storage_bits(a: np.ndarray):
 
 def make_layer(wl, inp):
     layer = MoELayer(wl.T, wl.d, wl.ffn, wl.E, wl.k, wl.capacity_factor, wl.gating, wl.act,
-                     wl.dtype, wl.ep_ranks, wl.placement, wl.n_shared, wl.ffn_shared)
+                     wl.dtype, wl.ep_ranks, wl.placement, wl.n_shared, wl.ffn_shared, aux_coef=wl.aux_coef)
     w = Weights(w_router=dev(inp.w_router), w1=dev(inp.w1), w2=dev(inp.w2), w_up=dev(inp.w_up),
                 bias=dev(inp.bias), ws_gate=dev(inp.ws_gate), ws_up=dev(inp.ws_up),
                 ws_down=dev(inp.ws_down))
@@ -138,6 +138,12 @@ def run_full_parity(wl, inp, dot_floor=False):
     errs["logits"] = assert_close("logits", g_logits, ref["logits_ref"], TOL_LOGITS)
     n = check_routing(wl, layer, ref, x_bits=storage_bits(inp.x))
     errs["topk_w"] = assert_close("topk_w", host(layer.topk_w), ref["topk_w"], 1e-5)
+    if wl.aux_coef:
+        # the balance loss and its logits gradient: fp32 sums over the GPU's own logits
+        errs["aux_loss"] = assert_close("aux_loss", host(layer.aux_loss), [ref["aux_loss"]], 1e-5)
+        errs["dlogits_aux"] = assert_close(
+            "dlogits_aux", host(layer.dlogits_aux),
+            oracle.balance_loss_grad(g_logits, ref["topk_idx"], wl.E, wl.aux_coef), 1e-5)
     errs["y"] = assert_close("y", host(layer.y), ref["y"], tol)
     if n > 0:
         errs["y_perm"] = assert_close("y_perm", host(layer.y_perm[:n]), ref["o_perm"], tol)

@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_plan", "moe_route", "moe_dispatch", "moe_expert_ffn_fwd", "moe_expert_ffn_bwd",
               "moe_combine", "moe_combine_bwd", "moe_route_bwd", "moe_dispatch_bwd",
+              "moe_aux_loss", "moe_aux_loss_bwd", "moe_dispatch_noalloc",
               "moe_status_string", "moe_last_hip_error"):
         assert n in names
 
@@ -111,7 +112,9 @@ def test_null_pointers_rejected_before_launch(lib):
     assert lib.moe_expert_ffn_bwd(cp, ctypes.byref(g), *([N] * 13)) == nat.MOE_ERR_INVALID
     assert lib.moe_combine(cp, *([N] * 6)) == nat.MOE_ERR_INVALID
     assert lib.moe_combine_bwd(cp, *([N] * 7)) == nat.MOE_ERR_INVALID
-    assert lib.moe_route_bwd(cp, *([N] * 8)) == nat.MOE_ERR_INVALID
+    assert lib.moe_route_bwd(cp, *([N] * 9)) == nat.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(cp, N, N, 0.01, N, N, N) == nat.MOE_ERR_INVALID
+    assert lib.moe_aux_loss_bwd(cp, N, N, 0.01, N, N) == nat.MOE_ERR_INVALID
     assert lib.moe_dispatch_bwd(cp, *([N] * 7)) == nat.MOE_ERR_INVALID
 
 

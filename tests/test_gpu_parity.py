@@ -130,6 +130,17 @@ FUZZ = {
                           gating="softmax_topk", act="gelu", dtype="bf16", seed=49),
     "T40000_d512_E8_dot2": W("T40000_d512_E8_dot2", T=40000, d=512, ffn=16, E=8, k=2, capacity_factor=1.0,
                              gating="softmax_topk_renorm", act="gelu", dtype="bf16", zipf_s=1.2, seed=50),
+    # the balance loss (pages' coefficients 0.01 and 0.1) with its gradient
+    # through dlogits, dW_r and dx: fp32, bf16 with 64 experts and shared
+    # experts, and a skewed routing whose loss is well above coef
+    "T777_E32_aux_f32": W("T777_E32_aux_f32", T=777, d=200, ffn=96, E=32, k=5, capacity_factor=1.3,
+                          gating="topk_softmax", act="gelu", dtype="f32", aux_coef=0.1, seed=52),
+    "T2000_E64_aux_shared": W("T2000_E64_aux_shared", T=2000, d=256, ffn=64, E=64, k=6, capacity_factor=0.0,
+                              gating="softmax_topk", act="swiglu", dtype="bf16", ep_ranks=8, n_shared=2,
+                              ffn_shared=32, aux_coef=0.01, seed=53),
+    "T4096_E8_aux_skew": W("T4096_E8_aux_skew", T=4096, d=512, ffn=128, E=8, k=2, capacity_factor=1.0,
+                           gating="softmax_topk_renorm", act="gelu", dtype="bf16", zipf_s=1.2, aux_coef=0.1,
+                           seed=54),
     # more than 128 blocks of 256 tokens: dispatch takes its separate scan
     # launch instead of the per-workgroup sums of the block counts
     "T40000_E64_scan": W("T40000_E64_scan", T=40000, d=32, ffn=16, E=64, k=6, capacity_factor=1.0,
@@ -151,6 +162,8 @@ def test_fuzz(name):
     print({k: f"{v:.2e}" for k, v in errs.items()}, "n =", ref["layout"]["n"], flush=True)
     if name == "T8192_E4_skew_splitk":  # the case is what its comment says
         assert list(np.asarray(ref["layout"]["kept_counts"])) == [8192, 8192, 0, 0]
+    if name == "T4096_E8_aux_skew":  # skewed routing: the loss is well above its balanced value
+        assert ref["aux_loss"] > 1.5 * wl.aux_coef
     if name == "T8192_E8_skew_runs":
         kept = np.asarray(ref["layout"]["kept_counts"])
         nz = int((kept > 0).sum())
