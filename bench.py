@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the whole step captured in one HIP graph instead of eager calls")
+    ap.add_argument("--pipeline", type=int, default=0, metavar="CHUNKS",
+                    help="time the step with the batch cut into CHUNKS token chunks on two streams")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
@@ -167,13 +169,15 @@ def main():
                 bias=dev(inp.bias), ws_gate=dev(inp.ws_gate), ws_up=dev(inp.ws_up), ws_down=dev(inp.ws_down))
     x, dy = dev(inp.x), dev(inp.dy)
     torch.cuda.synchronize()
+    run_step = lambda: layer.step(x, dy, w)  # noqa: E731
+    if args.pipeline:
+        run_step = lambda: layer.step_pipelined(x, dy, w, chunks=args.pipeline)  # noqa: E731
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        layer.step(x, dy, w)
+        run_step()
     torch.cuda.synchronize()
 
     # 1) whole steps, events only at the ends
-    run_step = lambda: layer.step(x, dy, w)  # noqa: E731
     if args.graph:
         graph = layer.capture_step(x, dy, w)
         run_step = graph.replay
@@ -202,6 +206,13 @@ def main():
     if wl.n_shared:
         stages.append(("shared_bwd", lambda: layer.shared_bwd(x, dy, w)))
     stages += [("route_bwd", lambda: layer.route_bwd(x)), ("dispatch_bwd", lambda: layer.dispatch_bwd(w))]
+    if args.pipeline:
+        # the two halves of the dispatch the pipelined step calls apart
+        from mixture_experts_layer_36_amd import api
+        stages += [("dispatch_layout", lambda: api.moe_dispatch(
+                        layer.cfg, None, layer.topk_idx, None, layer.row_of, layer.assign_of_row, layer.raw_counts,
+                        layer.expert_counts, layer.expert_offsets, layer.send_counts, layer.send_offsets, layer.ws)),
+                   ("permute", lambda: api.moe_permute(layer.cfg, x, layer.row_of, layer.x_perm))]
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
            for _ in range(args.steps)]
     for s in range(args.steps):
@@ -219,6 +230,9 @@ def main():
     alg = algorithmic(wl, n, T_kept)
     kernels = {}
     for name, ms in times.items():
+        if name not in alg:
+            kernels[name] = {"ms": round(ms, 4)}
+            continue
         a = alg[name]
         ent = {"ms": round(ms, 4)}
         if "bytes" in a:
@@ -260,6 +274,18 @@ def main():
         log(f"[bench] cpu baseline on {args.cpu_tokens} tokens")
         cpu = cpu_baseline(wl, inp, args.cpu_tokens)
 
+    pipeline = None
+    if args.pipeline:
+        # the pages' overlap model (tutorial, 通信优化方法 三): total = T_A +
+        # max(T_comm, T_B), with T_comm the bandwidth kernels the side stream
+        # takes, T_B the expert GEMMs, T_A the rest (routing and layout)
+        t_comm = sum(times[n_] for n_ in ("permute", "combine", "combine_bwd", "route_bwd", "dispatch_bwd"))
+        t_b = gemm_ms
+        t_a = times["route"] + times["dispatch_layout"]
+        pipeline = {"chunks": args.pipeline, "T_A_ms": round(t_a, 4), "T_comm_ms": round(t_comm, 4),
+                    "T_B_ms": round(t_b, 4), "model_ms": round(t_a + max(t_comm, t_b), 4),
+                    "serial_ms": round(t_a + t_comm + t_b, 4), "measured_ms": round(ms_step, 4)}
+
     result = {
         "metric": "MoE layer fwd+bwd tokens/s on 1 MI355X; grouped-GEMM % MFMA peak; permute GB/s",
         "value": round(wl.T / (ms_step * 1e-3), 1),
@@ -272,12 +298,14 @@ def main():
                    "capacity_factor": wl.capacity_factor, "gating": wl.gating, "act": wl.act,
                    "n_shared": wl.n_shared, "ffn_shared": wl.ffn_shared, "ep_ranks": wl.ep_ranks,
                    "rows_kept": n, "parallelism": "single GPU",
-                   "launch": "hip graph" if args.graph else "eager"},
+                   "launch": "hip graph" if args.graph else (
+                       f"eager, {args.pipeline} token chunks on two streams" if args.pipeline else "eager")},
         "grouped_gemm_frac_mfma": roofline["frac"],
         "permute_GBps": permute_gbs,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "pipeline": pipeline,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(result), flush=True)

@@ -106,6 +106,13 @@ typedef struct {
   int32_t use_placement;    /* 1: group g is send slot g, whose expert (and
                                weight set) follows cfg's placement; 0: group g
                                uses weight set g                                */
+  const int64_t* ends;      /* DEVICE [groups] or NULL.  Not NULL: group g owns
+                               rows [offsets[g], ends[g]) instead (disjoint
+                               sub-ranges, ascending by group, e.g. one token
+                               chunk of every expert's segment, from
+                               moe_chunk_rows).  Forward and the backward's
+                               data gradients only; weight gradients need
+                               whole groups (ends = NULL).                     */
 } moe_groups;
 
 /* Host only; no GPU is touched.  Sizes every caller-owned buffer up front,
@@ -152,13 +159,41 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   row_of [T*k] int32: row of assignment (t, j), -1 if dropped;
  *   assign_of_row [n_max] int32: t*k + j of each row (rows >= n untouched);
  *   x_perm [n_max, d] dtype: x_perm[row_of[t*k+j]] = x[t] (exact copy) —
- *     the all-to-all send buffer, segment q = rows of EP rank q.
+ *     the all-to-all send buffer, segment q = rows of EP rank q.  NULL (with
+ *     x NULL too) computes the layout only; moe_permute copies later.
  *   ws: moe_plan's workspace. */
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                  void* x_perm, int32_t* row_of, int32_t* assign_of_row,
                  int32_t* raw_counts, int32_t* expert_counts,
                  int64_t* expert_offsets, int32_t* send_counts,
                  int64_t* send_offsets, void* ws, void* stream);
+
+/* The row copy of moe_dispatch alone: x_perm[row_of[t*k+j]] = x[t] for every
+ * kept (t, j) of cfg->T tokens.  row_of holds rows of the whole x_perm, so a
+ * caller can copy one token chunk [t0, t1) by passing x + t0*d,
+ * row_of + t0*k and a config with T = t1 - t0 (moe_dispatch with x_perm NULL
+ * having laid out the whole batch): the tutorial's 通信优化方法 三 overlap of
+ * communication with computation, here a bandwidth kernel beside the expert
+ * GEMMs of another chunk (FlowMoE notes, 关键设计: pipelining over token
+ * chunks).  Errors: MOE_ERR_INVALID for a null or misaligned pointer. */
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* row_of,
+                void* x_perm, void* stream);
+
+/* Rows of token chunks in the dispatch layout.  The kept rows of each expert
+ * are its first C choosers in token order, so the tokens of chunk r,
+ * [token_bounds[r], token_bounds[r+1]), hold a contiguous sub-range of every
+ * expert's segment.  Writes chunk_rows [chunks+1, E] int64 (DEVICE): row r,
+ * slot s = the first row of chunk r in send slot s (row 0 = the segments'
+ * starts, row `chunks` = their ends), so chunk r's moe_groups table is
+ * offsets = chunk_rows + r*E, ends = chunk_rows + (r+1)*E.
+ *   topk_idx, row_of, expert_offsets: moe_route's and moe_dispatch's;
+ *   token_bounds: HOST [chunks+1], ascending, 0 first and cfg->T last.
+ * Deterministic (integer atomic minimums).  Errors: MOE_ERR_INVALID for a
+ * null pointer or bad bounds, MOE_ERR_UNSUPPORTED for more than 16 chunks. */
+int moe_chunk_rows(const moe_config* cfg, const int32_t* topk_idx,
+                   const int32_t* row_of, const int64_t* expert_offsets,
+                   int64_t chunks, const int64_t* token_bounds,
+                   int64_t* chunk_rows, void* stream);
 
 /* moe_dispatch without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
@@ -191,6 +226,23 @@ int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,
                        const void* w_out, void* act_saved, void* h,
                        void* y_rows, void* stream);
 
+/* The two halves of moe_expert_ffn_bwd, for callers that pipeline token
+ * chunks: moe_expert_ffn_bwd_data computes dL/d act (into ws) and dx_rows for
+ * the group table's rows (sub-ranges allowed: grp->ends), and
+ * moe_expert_ffn_bwd_weights the weight gradients over whole groups (ends
+ * NULL) from the dL/d act that data calls covering every row left in ws.
+ * Nothing else may use ws in between.  Arguments, results and errors as in
+ * moe_expert_ffn_bwd. */
+int moe_expert_ffn_bwd_data(const moe_config* cfg, const moe_groups* grp,
+                            const void* w_in, const void* w_up,
+                            const void* w_out, const void* act_saved,
+                            const void* dy_rows, void* dx_rows, void* ws,
+                            void* stream);
+int moe_expert_ffn_bwd_weights(const moe_config* cfg, const moe_groups* grp,
+                               const void* x_rows, const void* h,
+                               const void* dy_rows, void* dw_in, void* dw_up,
+                               void* dw_out, void* ws, void* stream);
+
 /* Grouped expert FFN backward (tutorial: 专家并行与数据并行的结合 三.3:
  * gradients routed back to the experts, parameter gradients computed
  * locally).  dy_rows [rows_max, d] is dL/d y_rows.
@@ -201,7 +253,8 @@ int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,
  *       fp32 partials of weight gradients split over their rows).
  * Errors: MOE_ERR_INVALID also when the group table would need more
  *   workspace than moe_plan's workspace_bytes for cfg (a table with more
- *   groups, rows or hidden width than the routed or shared tables above). */
+ *   groups, rows or hidden width than the routed or shared tables above), or
+ *   has sub-range ends (the weight gradients need whole groups). */
 int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp,
                        const void* x_rows, const void* w_in, const void* w_up,
                        const void* w_out, const void* act_saved, const void* h,

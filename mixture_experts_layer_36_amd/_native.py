@@ -37,7 +37,7 @@ class MoeSizes(ctypes.Structure):
 class MoeGroups(ctypes.Structure):
     _fields_ = [("groups", ctypes.c_int64), ("ffn", ctypes.c_int64),
                 ("rows_max", ctypes.c_int64), ("offsets", ctypes.c_void_p),
-                ("use_placement", ctypes.c_int32)]
+                ("use_placement", ctypes.c_int32), ("ends", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -51,6 +51,10 @@ SIGNATURES = {
     "moe_dispatch_noalloc": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn_fwd": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn_bwd": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_ffn_bwd_data": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_ffn_bwd_weights": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_permute": [_CFG, _P, _P, _P, _P],
+    "moe_chunk_rows": [_CFG, _P, _P, _P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), _P, _P],
     "moe_combine": [_CFG, _P, _P, _P, _P, _P, _P],
     "moe_combine_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P],
     "moe_route_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P],

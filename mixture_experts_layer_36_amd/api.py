@@ -28,11 +28,12 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def groups(n_groups: int, ffn: int, rows_max: int, offsets: torch.Tensor, use_placement: bool) -> MoeGroups:
-    if offsets.dtype != torch.int64:
+def groups(n_groups: int, ffn: int, rows_max: int, offsets: torch.Tensor, use_placement: bool,
+           ends: torch.Tensor = None) -> MoeGroups:
+    if offsets.dtype != torch.int64 or (ends is not None and ends.dtype != torch.int64):
         raise ValueError("group offsets are int64")
     return MoeGroups(groups=n_groups, ffn=ffn, rows_max=rows_max, offsets=_ptr(offsets),
-                     use_placement=1 if use_placement else 0)
+                     use_placement=1 if use_placement else 0, ends=_ptr(ends))
 
 
 def moe_route(cfg, x, w_router, bias, logits, topk_idx, topk_w, ws, stream=None):
@@ -64,6 +65,28 @@ def moe_expert_ffn_bwd(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_row
     call("moe_expert_ffn_bwd", ctypes.byref(cfg), ctypes.byref(grp), _ptr(x_rows), _ptr(w_in),
          _ptr(w_up), _ptr(w_out), _ptr(act_saved), _ptr(h), _ptr(dy_rows), _ptr(dx_rows),
          _ptr(dw_in), _ptr(dw_up), _ptr(dw_out), _ptr(ws), _stream(stream))
+
+
+def moe_expert_ffn_bwd_data(cfg, grp, w_in, w_up, w_out, act_saved, dy_rows, dx_rows, ws, stream=None):
+    call("moe_expert_ffn_bwd_data", ctypes.byref(cfg), ctypes.byref(grp), _ptr(w_in), _ptr(w_up), _ptr(w_out),
+         _ptr(act_saved), _ptr(dy_rows), _ptr(dx_rows), _ptr(ws), _stream(stream))
+
+
+def moe_expert_ffn_bwd_weights(cfg, grp, x_rows, h, dy_rows, dw_in, dw_up, dw_out, ws, stream=None):
+    call("moe_expert_ffn_bwd_weights", ctypes.byref(cfg), ctypes.byref(grp), _ptr(x_rows), _ptr(h),
+         _ptr(dy_rows), _ptr(dw_in), _ptr(dw_up), _ptr(dw_out), _ptr(ws), _stream(stream))
+
+
+def moe_permute(cfg, x, row_of, x_perm, stream=None):
+    call("moe_permute", ctypes.byref(cfg), _ptr(x), _ptr(row_of), _ptr(x_perm), _stream(stream))
+
+
+def moe_chunk_rows(cfg, topk_idx, row_of, expert_offsets, token_bounds, chunk_rows, stream=None):
+    """token_bounds: host sequence of chunks + 1 token indices."""
+    n = len(token_bounds) - 1
+    bounds = (ctypes.c_int64 * (n + 1))(*[int(b) for b in token_bounds])
+    call("moe_chunk_rows", ctypes.byref(cfg), _ptr(topk_idx), _ptr(row_of), _ptr(expert_offsets),
+         ctypes.c_int64(n), bounds, _ptr(chunk_rows), _stream(stream))
 
 
 def moe_combine(cfg, y_perm, row_of, topk_w, y_shared, y, stream=None):

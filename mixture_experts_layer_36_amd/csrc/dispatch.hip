@@ -318,6 +318,76 @@ static void launch_permute_copy(const DispatchArgs& a, hipStream_t st) {
   else launch_permute_copy_k<T, 8>(a, st);
 }
 
+hipError_t launch_permute(const DispatchArgs& a, bool bf16_dtype, hipStream_t st) {
+  if (bf16_dtype) launch_permute_copy<bf16>(a, st);
+  else launch_permute_copy<float>(a, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Rows of token chunks.  With the layout above, the kept rows of expert e
+// are its first C choosers in token order, so the tokens of a chunk
+// [t_r, t_{r+1}) occupy a contiguous sub-range of each expert's segment:
+// rows [b_r, b_{r+1}) with b_r = the first kept row of e chosen by a token
+// t >= t_r (the segment's end if none).  chunk_rows[r][s] = b_r of send slot
+// s: the group tables of the chunks (offsets = row r, ends = row r + 1).
+// Three launches: fill every row with the segment ends (row 0 with the
+// starts), an integer atomicMin per kept assignment (order independent, so
+// deterministic), then a suffix minimum over the chunks so that a chunk
+// without rows of e starts where the next one does.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int slot_of_expert(int e, int E, int R, int placement) {
+  const int L = E / R;
+  return placement == 0 ? e : (e % R) * L + e / R;
+}
+
+__global__ __launch_bounds__(64) void chunk_rows_init_kernel(const int64_t* __restrict__ offsets, int E,
+                                                             int chunks, int64_t* __restrict__ rows) {
+  for (int i = threadIdx.x; i < (chunks + 1) * E; i += 64) {
+    const int r = i / E, s = i - r * E;
+    rows[i] = r == 0 ? offsets[s] : offsets[s + 1];
+  }
+}
+
+__global__ __launch_bounds__(256) void chunk_rows_min_kernel(const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ row_of, int64_t Tn, int E,
+                                                             int k, int R, int placement, ChunkBounds cb,
+                                                             int64_t* __restrict__ rows) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // assignment t * k + j
+  if (i >= Tn * k) return;
+  const int32_t row = row_of[i];
+  if (row < 0) return;
+  const int64_t t = i / k;
+  int r = 0;
+  while (r + 1 < cb.chunks && t >= cb.t[r + 1]) ++r;
+  if (r == 0) return;  // row 0 holds the segment starts already
+  const int s = slot_of_expert(idx[i], E, R, placement);
+  atomicMin((unsigned long long*)&rows[(int64_t)r * E + s], (unsigned long long)row);
+}
+
+__global__ __launch_bounds__(64) void chunk_rows_suffix_kernel(int E, int chunks, int64_t* __restrict__ rows) {
+  for (int s = threadIdx.x; s < E; s += 64)
+    for (int r = chunks - 1; r >= 1; --r) {
+      const int64_t nxt = rows[(int64_t)(r + 1) * E + s];
+      if (nxt < rows[(int64_t)r * E + s]) rows[(int64_t)r * E + s] = nxt;
+    }
+}
+
+hipError_t launch_chunk_rows(const ChunkRowsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(chunk_rows_init_kernel, dim3(1), dim3(64), 0, st, a.expert_offsets, a.E, a.cb.chunks, a.rows);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n = a.T * a.k;
+  if (a.cb.chunks > 1 && n > 0) {
+    hipLaunchKernelGGL(chunk_rows_min_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.topk_idx,
+                       a.row_of, a.T, a.E, a.k, a.R, a.placement, a.cb, a.rows);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(chunk_rows_suffix_kernel, dim3(1), dim3(64), 0, st, a.E, a.cb.chunks, a.rows);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st) {
   const int nb = (int)((a.T + kDispatchBlock - 1) / kDispatchBlock);
   hipLaunchKernelGGL(block_hist_kernel, dim3(nb), dim3(kDispatchBlock), 0, st, a.topk_idx, a.T, a.E, a.k,
@@ -342,9 +412,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t s
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (bf16_dtype) launch_permute_copy<bf16>(a, st);
-  else launch_permute_copy<float>(a, st);
-  return hipGetLastError();
+  if (!a.x_perm) return hipSuccess;  // layout only
+  return launch_permute(a, bf16_dtype, st);
 }
 
 }  // namespace moe

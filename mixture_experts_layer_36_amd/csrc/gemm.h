@@ -29,6 +29,7 @@ struct Args {
   const void* X1 = nullptr; int64_t ldx = 0;
   int64_t M = 0, N = 0, K = 0;
   const int64_t* offsets = nullptr;  // device [groups+1]
+  const int64_t* ends = nullptr;     // device [groups] or null: row-split groups own [offsets[g], ends[g])
   int groups = 0;
   int rr_R = 0, rr_L = 1;   // round-robin slot -> expert map (rr_R = 0: identity)
   int tiles_m = 0, tiles_n = 0;

@@ -65,20 +65,26 @@ MOE_HD void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt, i
 // count, since the per-group row counts live on the device.  Each workgroup
 // counts the BM-row tiles the groups really hold; surplus workgroups exit,
 // and the XCD remap and the grouped order run over the real tiles only.
-// Returns false for a surplus workgroup; else group g, its rows
-// [row_begin, row_end) from the tile's first row, and the column tile nt.
+// Group g owns rows [offsets[g], offsets[g + 1]), or [offsets[g], ends[g])
+// when ends is given (disjoint sub-ranges, e.g. one token chunk of every
+// expert's segment).  Returns false for a surplus workgroup; else group g,
+// its rows [row_begin, row_end) from the tile's first row, and the column
+// tile nt.
+MOE_HD int64_t group_end(const int64_t* offsets, const int64_t* ends, int g) {
+  return ends ? ends[g] : offsets[g + 1];
+}
 template <int BM>
-MOE_HD bool row_tile_of(const int64_t* offsets, int groups, int tiles_n, int gm, int hw, int& g, int64_t& row_begin,
-                        int64_t& row_end, int& nt) {
+MOE_HD bool row_tile_of(const int64_t* offsets, const int64_t* ends, int groups, int tiles_n, int gm, int hw, int& g,
+                        int64_t& row_begin, int64_t& row_end, int& nt) {
   int real_m = 0;
-  for (int gg = 0; gg < groups; ++gg) real_m += (int)((offsets[gg + 1] - offsets[gg] + BM - 1) / BM);
+  for (int gg = 0; gg < groups; ++gg) real_m += (int)((group_end(offsets, ends, gg) - offsets[gg] + BM - 1) / BM);
   const int real = real_m * tiles_n;
   if (hw >= real) return false;
   int mt;
   grouped_order(xcd_remap(hw, real), real_m, tiles_n, mt, nt, gm);
   int acc_t = 0;
   for (int gg = 0; gg < groups; ++gg) {
-    const int64_t o0 = offsets[gg], o1 = offsets[gg + 1];
+    const int64_t o0 = offsets[gg], o1 = group_end(offsets, ends, gg);
     const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
     if (mt < acc_t + nt_g) {
       g = gg;

@@ -88,8 +88,8 @@ struct StageRes {
 template <int BM>
 __device__ __forceinline__ bool row_tile_of(const gemm::Args& a, int& g, int64_t& row_begin, int64_t& row_end,
                                             int& nt) {
-  return gemm_addr::row_tile_of<BM>(a.offsets, a.groups, a.tiles_n, a.gm, (int)blockIdx.x, g, row_begin, row_end,
-                                    nt);
+  return gemm_addr::row_tile_of<BM>(a.offsets, a.ends, a.groups, a.tiles_n, a.gm, (int)blockIdx.x, g, row_begin,
+                                    row_end, nt);
 }
 
 __device__ __forceinline__ float gelu_f(float z) {

@@ -24,6 +24,20 @@ struct DispatchArgs {
   int64_t T; int64_t d; int E; int k; int64_t C; int R; int placement;
 };
 
+// Token chunks [t[r], t[r + 1]) for r < chunks, t[0] = 0, t[chunks] = T.
+constexpr int kMaxChunks = 16;
+struct ChunkBounds {
+  int64_t t[kMaxChunks + 1];
+  int chunks;
+};
+
+struct ChunkRowsArgs {
+  const int32_t* topk_idx; const int32_t* row_of; const int64_t* expert_offsets;
+  int64_t* rows;  // [chunks + 1][E]
+  ChunkBounds cb;
+  int64_t T; int E; int k; int R; int placement;
+};
+
 struct CombineArgs {
   const void* y_perm; const int32_t* row_of; const float* topk_w;
   const void* y_shared; void* y;                 // forward
@@ -55,7 +69,9 @@ struct AuxArgs {
 hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st);
 // bytes of ws the bf16 route uses for its re-packed copy of w_router
 size_t route_ws_bytes(int64_t d, int64_t E);
-hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st);
+hipError_t launch_dispatch(const DispatchArgs& a, bool bf16_dtype, hipStream_t st);  // x_perm null: layout only
+hipError_t launch_permute(const DispatchArgs& a, bool bf16_dtype, hipStream_t st);   // the row copy alone
+hipError_t launch_chunk_rows(const ChunkRowsArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_combine_bwd(const CombineArgs& a, bool bf16_dtype, hipStream_t st);
 hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t st);

@@ -9,6 +9,7 @@
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <initializer_list>
 #include <mutex>
 #include <type_traits>
 
@@ -139,6 +140,7 @@ int check_groups(const moe_config* c, const moe_groups* g) {
 void fill_placement(const moe_config* c, const moe_groups* g, moe::gemm::Args& a) {
   a.groups = (int)g->groups;
   a.offsets = g->offsets;
+  a.ends = g->ends;
   if (g->use_placement && c->placement == MOE_PLACE_ROUND_ROBIN && c->ep_ranks > 1) {
     a.rr_R = c->ep_ranks;
     a.rr_L = (int)(c->E / c->ep_ranks);
@@ -172,10 +174,10 @@ hipError_t ffn_fwd(const moe_config* c, const moe_groups* g, const void* x, cons
   return run_rows<T>(KIND_FWD, EPI_STORE, a2, g->rows_max, st);
 }
 
+// Data gradients: dL/d act into ws (rows as in the row buffers), then dx.
 template <typename T>
-hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, const void* w_in, const void* w_up,
-                   const void* w_out, const void* act_saved, const void* h, const void* dy, void* dx, void* dw_in,
-                   void* dw_up, void* dw_out, void* ws, hipStream_t st) {
+hipError_t ffn_bwd_data(const moe_config* c, const moe_groups* g, const void* w_in, const void* w_up,
+                        const void* w_out, const void* act_saved, const void* dy, void* dx, void* ws, hipStream_t st) {
   using namespace moe::gemm;
   const int64_t d = c->d, F = g->ffn;
   const bool swiglu = c->act == MOE_ACT_SWIGLU;
@@ -200,8 +202,18 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
   a2.b_split = swiglu ? F : 0;
   a2.N = d; a2.K = m * F;
   a2.C = dx; a2.ldc = d;
-  e = run_rows<T>(KIND_DGRAD, EPI_STORE, a2, g->rows_max, st);
-  if (e != hipSuccess) return e;
+  return run_rows<T>(KIND_DGRAD, EPI_STORE, a2, g->rows_max, st);
+}
+
+// Weight gradients over whole groups, from dL/d act in ws.
+template <typename T>
+hipError_t ffn_bwd_weights(const moe_config* c, const moe_groups* g, const void* x, const void* h, const void* dy,
+                           void* dw_in, void* dw_up, void* dw_out, void* ws, hipStream_t st) {
+  using namespace moe::gemm;
+  const int64_t d = c->d, F = g->ffn;
+  const bool swiglu = c->act == MOE_ACT_SWIGLU;
+  const int64_t m = swiglu ? 2 : 1;
+  hipError_t e;
   // Launches with few tiles split their reduction (bf16), with fp32 partials
   // placed after d_act in ws, as long as the workspace moe_plan sized holds
   // them (it does for the routed call over all experts and the shared call).
@@ -232,6 +244,32 @@ hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, cons
     a4.partial = partial;
   }
   return run_wgrad<T>(swiglu ? EPI_STORE_SPLITN : EPI_STORE, a4, st);
+}
+
+template <typename T>
+hipError_t ffn_bwd(const moe_config* c, const moe_groups* g, const void* x, const void* w_in, const void* w_up,
+                   const void* w_out, const void* act_saved, const void* h, const void* dy, void* dx, void* dw_in,
+                   void* dw_up, void* dw_out, void* ws, hipStream_t st) {
+  hipError_t e = ffn_bwd_data<T>(c, g, w_in, w_up, w_out, act_saved, dy, dx, ws, st);
+  if (e != hipSuccess) return e;
+  return ffn_bwd_weights<T>(c, g, x, h, dy, dw_in, dw_up, dw_out, ws, st);
+}
+
+// Pointer checks shared by the FFN backward entry points: every pointer of
+// `req` present and 16-byte aligned, ws 256-byte aligned and large enough
+// for the group table's dL/d act and split partials.
+int check_ffn_bwd_ptrs(const moe_config* cfg, const moe_groups* grp, std::initializer_list<const void*> req,
+                       void* ws) {
+  for (const void* p : req)
+    if (!p) return MOE_ERR_INVALID;
+  for (const void* p : req)
+    if (!aligned16(p)) return MOE_ERR_INVALID;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID;
+  // the group table's workspace (dL/d act, then split partials) must fit in
+  // moe_plan's workspace_bytes: the routed and shared tables always do
+  if (ffn_bwd_ws(cfg, grp->groups, grp->ffn, grp->rows_max) > ws_layout(cfg, plan_n_max(cfg)).total)
+    return MOE_ERR_INVALID;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -310,10 +348,11 @@ int check_dispatch_args(const moe_config* cfg, const void* x, const int32_t* top
                         int64_t* expert_offsets, int32_t* send_counts, int64_t* send_offsets) {
   int s = check_config(cfg);
   if (s != MOE_OK) return s;
-  if (!x || !topk_idx || !x_perm || !row_of || !assign_of_row || !raw_counts || !expert_counts || !expert_offsets ||
-      !send_counts || !send_offsets)
+  if (!topk_idx || !row_of || !assign_of_row || !raw_counts || !expert_counts || !expert_offsets || !send_counts ||
+      !send_offsets)
     return MOE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID;
+  // x_perm NULL: layout only (x unused); else x is copied into it
+  if (x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -349,6 +388,37 @@ int moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* to
                        send_counts, send_offsets, w, kNoAllocCntBytes, stream);
 }
 
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* row_of, void* x_perm, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!x || !row_of || !x_perm) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID;
+  moe::DispatchArgs a{};
+  a.x = x; a.row_of = const_cast<int32_t*>(row_of); a.x_perm = x_perm;  // read only by the copy
+  a.T = cfg->T; a.d = cfg->d; a.E = (int)cfg->E; a.k = (int)cfg->k;
+  return hip_status(moe::launch_permute(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_chunk_rows(const moe_config* cfg, const int32_t* topk_idx, const int32_t* row_of,
+                   const int64_t* expert_offsets, int64_t chunks, const int64_t* token_bounds, int64_t* chunk_rows,
+                   void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!topk_idx || !row_of || !expert_offsets || !token_bounds || !chunk_rows) return MOE_ERR_INVALID;
+  if (chunks < 1) return MOE_ERR_INVALID;
+  if (chunks > moe::kMaxChunks) return MOE_ERR_UNSUPPORTED;
+  moe::ChunkRowsArgs a{};
+  if (token_bounds[0] != 0 || token_bounds[chunks] != cfg->T) return MOE_ERR_INVALID;
+  for (int64_t r = 0; r <= chunks; ++r) {
+    if (r > 0 && token_bounds[r] < token_bounds[r - 1]) return MOE_ERR_INVALID;
+    a.cb.t[r] = token_bounds[r];
+  }
+  a.cb.chunks = (int)chunks;
+  a.topk_idx = topk_idx; a.row_of = row_of; a.expert_offsets = expert_offsets; a.rows = chunk_rows;
+  a.T = cfg->T; a.E = (int)cfg->E; a.k = (int)cfg->k; a.R = cfg->ep_ranks; a.placement = cfg->placement;
+  return hip_status(moe::launch_chunk_rows(a, (hipStream_t)stream));
+}
+
 int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* w_in,
                        const void* w_up, const void* w_out, void* act_saved, void* h, void* y_rows, void* stream) {
   int s = check_config(cfg);
@@ -373,25 +443,53 @@ int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp, const void*
   if (s != MOE_OK) return s;
   s = check_groups(cfg, grp);
   if (s != MOE_OK) return s;
+  if (grp->ends) return MOE_ERR_INVALID;  // weight gradients need whole groups
   const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
-  if (!x_rows || !w_in || !w_out || !act_saved || !h || !dy_rows || !dx_rows || !dw_in || !dw_out || !ws ||
-      (swiglu && (!w_up || !dw_up)))
-    return MOE_ERR_INVALID;
-  const void* ptrs[] = {x_rows, w_in, w_out, act_saved, h, dy_rows, dx_rows, dw_in, dw_out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MOE_ERR_INVALID;
-  if (swiglu && (!aligned16(w_up) || !aligned16(dw_up))) return MOE_ERR_INVALID;
-  if ((uintptr_t)ws & 255u) return MOE_ERR_INVALID;
-  // the group table's workspace (dL/d act, then split partials) must fit in
-  // moe_plan's workspace_bytes: the routed and shared tables always do
-  if (ffn_bwd_ws(cfg, grp->groups, grp->ffn, grp->rows_max) > ws_layout(cfg, plan_n_max(cfg)).total)
-    return MOE_ERR_INVALID;
+  s = check_ffn_bwd_ptrs(cfg, grp,
+                         {x_rows, w_in, w_out, act_saved, h, dy_rows, dx_rows, dw_in, dw_out, swiglu ? w_up : w_in,
+                          swiglu ? dw_up : dw_in},
+                         ws);
+  if (s != MOE_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = cfg->dtype == MOE_BF16
                      ? ffn_bwd<moe::bf16>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,
                                           dw_up, dw_out, ws, st)
                      : ffn_bwd<float>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,
                                       dw_up, dw_out, ws, st);
+  return hip_status(e);
+}
+
+int moe_expert_ffn_bwd_data(const moe_config* cfg, const moe_groups* grp, const void* w_in, const void* w_up,
+                            const void* w_out, const void* act_saved, const void* dy_rows, void* dx_rows, void* ws,
+                            void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  s = check_groups(cfg, grp);
+  if (s != MOE_OK) return s;
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  s = check_ffn_bwd_ptrs(cfg, grp, {w_in, w_out, act_saved, dy_rows, dx_rows, swiglu ? w_up : w_in}, ws);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MOE_BF16
+                     ? ffn_bwd_data<moe::bf16>(cfg, grp, w_in, w_up, w_out, act_saved, dy_rows, dx_rows, ws, st)
+                     : ffn_bwd_data<float>(cfg, grp, w_in, w_up, w_out, act_saved, dy_rows, dx_rows, ws, st);
+  return hip_status(e);
+}
+
+int moe_expert_ffn_bwd_weights(const moe_config* cfg, const moe_groups* grp, const void* x_rows, const void* h,
+                               const void* dy_rows, void* dw_in, void* dw_up, void* dw_out, void* ws, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  s = check_groups(cfg, grp);
+  if (s != MOE_OK) return s;
+  if (grp->ends) return MOE_ERR_INVALID;  // weight gradients need whole groups
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  s = check_ffn_bwd_ptrs(cfg, grp, {x_rows, h, dy_rows, dw_in, dw_out, swiglu ? dw_up : dw_in}, ws);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MOE_BF16
+                     ? ffn_bwd_weights<moe::bf16>(cfg, grp, x_rows, h, dy_rows, dw_in, dw_up, dw_out, ws, st)
+                     : ffn_bwd_weights<float>(cfg, grp, x_rows, h, dy_rows, dw_in, dw_up, dw_out, ws, st);
   return hip_status(e);
 }
 

@@ -177,6 +177,111 @@ class MoELayer:
         self.forward(x, w)
         self.backward(x, dy, w)
 
+    # ------------------------------------------------------------ pipelined
+    def _pipeline_setup(self, chunks):
+        """Per-chunk configs (the same layer over a token range, for the
+        token-range calls; the expert FFN calls keep the layer's config, as
+        their group tables address the whole row buffers) and buffers:
+        the chunk row table, a second workspace for the side stream's router
+        backward, the side stream and its events."""
+        if getattr(self, "_pipe_chunks", None) == chunks:
+            return
+        T, E = self.T, self.E
+        self._bounds = [T * r // chunks for r in range(chunks + 1)]
+        self._ccfg = [make_config(self._bounds[r + 1] - self._bounds[r], self.d, self.F, E, self.k,
+                                  self.cfg.capacity_factor, self.cfg.gating, self.cfg.act, self.cfg.dtype,
+                                  self.R, self.cfg.placement, self.cfg.n_shared, self.cfg.ffn_shared)
+                      for r in range(chunks)]
+        self.chunk_rows = torch.empty((chunks + 1) * E, dtype=torch.int64, device=self.device)
+        n = self.sizes.n_max
+        self._cgrp = [api.groups(E, self.F, n, self.chunk_rows[r * E:(r + 1) * E], True,
+                                 ends=self.chunk_rows[(r + 1) * E:(r + 2) * E]) for r in range(chunks)]
+        self.ws2 = torch.empty_like(self.ws)
+        self._side = torch.cuda.Stream(device=self.device)
+        self._pipe_chunks = chunks
+
+    def step_pipelined(self, x, dy, w: Weights, chunks=2):
+        """One step with the batch cut into `chunks` token chunks on two
+        streams (FlowMoE notes, 关键设计: pipelining over token chunks;
+        tutorial, 通信优化方法 三: overlap communication with computation).
+        The bandwidth kernels of a chunk (permute, combine, combine backward,
+        dispatch backward) run on a side stream beside the expert GEMMs of
+        the other chunks on the main stream.
+
+        Routing and the dispatch layout cover the whole batch first (every
+        expert's segment start needs every token's choice); since each
+        expert's kept rows are in token order, chunk r owns a contiguous
+        sub-range of every segment (moe_chunk_rows), so the chunks' GEMMs
+        run on sub-range group tables over the same buffers, and the weight
+        gradients once over whole groups.  Every output is bit-identical to
+        step().  The backward starts after the forward has finished, as it
+        would when dy arrives from the next layer."""
+        chunks = max(1, min(int(chunks), self.T, 16))
+        self._pipeline_setup(chunks)
+        main, side = torch.cuda.current_stream(), self._side
+        k, b = self.k, self._bounds
+        ev = lambda: torch.cuda.Event()  # noqa: E731
+
+        def rec(stream):
+            e = ev()
+            e.record(stream)
+            return e
+
+        # forward: whole-batch routing and layout, then the chunks
+        self.route(x, w)
+        api.moe_dispatch(self.cfg, None, self.topk_idx, None, self.row_of, self.assign_of_row, self.raw_counts,
+                         self.expert_counts, self.expert_offsets, self.send_counts, self.send_offsets, self.ws, main)
+        if self.aux_coef:
+            self.aux_fwd()
+        api.moe_chunk_rows(self.cfg, self.topk_idx, self.row_of, self.expert_offsets, b, self.chunk_rows, main)
+        side.wait_event(rec(main))
+        perm = []
+        for r in range(chunks):
+            api.moe_permute(self._ccfg[r], x[b[r]:b[r + 1]], self.row_of[b[r] * k:b[r + 1] * k], self.x_perm, side)
+            perm.append(rec(side))
+        if self.n_shared:
+            self.shared_fwd(x, w)
+        ffn = []
+        for r in range(chunks):
+            main.wait_event(perm[r])
+            api.moe_expert_ffn_fwd(self.cfg, self._cgrp[r], self.x_perm, w.w1, w.w_up, w.w2, self.act_saved,
+                                   self.h, self.y_perm, main)
+            ffn.append(rec(main))
+        for r in range(chunks):
+            side.wait_event(ffn[r])
+            api.moe_combine(self._ccfg[r], self.y_perm, self.row_of[b[r] * k:b[r + 1] * k],
+                            self.topk_w[b[r]:b[r + 1]], self.y_shared[b[r]:b[r + 1]] if self.n_shared else None,
+                            self.y[b[r]:b[r + 1]], side)
+        # the forward is complete before the backward starts
+        main.wait_event(rec(side))
+        side.wait_event(rec(main))
+        cb = []
+        for r in range(chunks):
+            api.moe_combine_bwd(self._ccfg[r], dy[b[r]:b[r + 1]], self.y_perm, self.row_of[b[r] * k:b[r + 1] * k],
+                                self.topk_w[b[r]:b[r + 1]], self.dy_perm, self.d_topk_w[b[r]:b[r + 1]], side)
+            cb.append(rec(side))
+        if self.aux_coef:
+            api.moe_aux_loss_bwd(self.cfg, self.logits, self.raw_counts, self.aux_coef, self.dlogits_aux, side)
+        api.moe_route_bwd(self.cfg, x, self.logits, self.topk_idx, self.d_topk_w,
+                          self.dlogits_aux if self.aux_coef else None, self.dlogits, self.dw_router, self.ws2, side)
+        if self.n_shared:
+            self.shared_bwd(x, dy, w)
+        dg = []
+        for r in range(chunks):
+            main.wait_event(cb[r])
+            api.moe_expert_ffn_bwd_data(self.cfg, self._cgrp[r], w.w1, w.w_up, w.w2, self.act_saved,
+                                        self.dy_perm, self.dx_perm, self.ws, main)
+            dg.append(rec(main))
+        api.moe_expert_ffn_bwd_weights(self.cfg, self.grp, self.x_perm, self.h, self.dy_perm, self.dw1, self.dw_up,
+                                       self.dw2, self.ws, main)
+        for r in range(chunks):
+            side.wait_event(dg[r])
+            api.moe_dispatch_bwd(self._ccfg[r], self.dx_perm, self.row_of[b[r] * k:b[r + 1] * k],
+                                 self.dlogits[b[r]:b[r + 1]], w.w_router,
+                                 self.dx_shared[b[r]:b[r + 1]] if self.n_shared else None, self.dx[b[r]:b[r + 1]],
+                                 side)
+        main.wait_event(rec(side))
+
     def capture_step(self, x, dy, w: Weights):
         """Record one whole step (every entry point, forward and backward) into
         a HIP graph; replaying it re-runs the step on the same buffers, with

@@ -19,7 +19,10 @@
 //   * the row-split launches map their real tiles one to one onto workgroups.
 //
 // Input (stdin), one FFN call:  d F swiglu groups rows_max rr_R rr_L
-// followed by groups+1 offsets.  Output: "OK <loads checked>" or the first
+// followed by groups+1 offsets, and optionally a chunk count followed by
+// chunks+1 rows of per-group bounds (token chunks of every group: the
+// row-split launches are then also checked once per chunk on the sub-ranges
+// [bounds[r][g], bounds[r+1][g])).  Output: "OK <loads checked>" or the first
 // violation, exit status 1.
 #include <hip/hip_runtime.h>
 
@@ -126,13 +129,14 @@ struct RowsLaunch {
   int64_t lda, ldb, gstride, N, K, b_split;
 };
 
-void check_rows(const RowsLaunch& L, const std::vector<int64_t>& off, int groups, int64_t rows_max, int rr_R,
-                int rr_L, int weight_sets) {
+// ends: null (group g owns [off[g], off[g + 1])) or [groups] sub-range ends.
+void check_rows(const RowsLaunch& L, const std::vector<int64_t>& off, const int64_t* ends, int groups,
+                int64_t rows_max, int rr_R, int rr_L, int weight_sets) {
   int tiles_m, tiles_n;
   rows_tiles(L.N, L.pair ? BN / 2 : BN, rows_max, groups, BM, tiles_m, tiles_n);
   const int64_t grid = (int64_t)tiles_m * tiles_n;
   int real_m = 0;
-  for (int g = 0; g < groups; ++g) real_m += (int)((off[g + 1] - off[g] + BM - 1) / BM);
+  for (int g = 0; g < groups; ++g) real_m += (int)((group_end(off.data(), ends, g) - off[g] + BM - 1) / BM);
   std::set<std::tuple<int, int64_t, int>> seen;
   const int real = real_m * tiles_n;
   const int every = real > 600 ? real / 600 : 1;
@@ -141,13 +145,14 @@ void check_rows(const RowsLaunch& L, const std::vector<int64_t>& off, int groups
   for (int hw = 0; hw < grid; ++hw) {
     int g = -1, nt = 0;
     int64_t rb = 0, re = 0;
-    if (!row_tile_of<BM>(off.data(), groups, tiles_n, 8, hw, g, rb, re, nt)) {
+    if (!row_tile_of<BM>(off.data(), ends, groups, tiles_n, 8, hw, g, rb, re, nt)) {
       if (hw < real) fail(std::string(L.name) + ": a real tile's workgroup exits");
       continue;
     }
     if (hw >= real) fail(std::string(L.name) + ": a surplus workgroup takes a tile");
     if (!seen.insert({g, rb, nt}).second) fail(std::string(L.name) + ": two workgroups take one tile");
-    if (rb < off[g] || rb >= off[g + 1] || re != off[g + 1] || (rb - off[g]) % BM != 0)
+    const int64_t gend = group_end(off.data(), ends, g);
+    if (rb < off[g] || rb >= gend || re != gend || (rb - off[g]) % BM != 0)
       fail(std::string(L.name) + ": tile rows outside its group");
     const int wi = weight_index(g, rr_R, rr_L);
     if (wi < 0 || wi >= weight_sets) fail(std::string(L.name) + ": weight set out of range");
@@ -267,31 +272,55 @@ void check_wgrad(const WgradLaunch& L, const std::vector<int64_t>& off, int grou
 int main() {
   long long d, F, swiglu, groups, rows_max, rr_R, rr_L;
   if (std::scanf("%lld %lld %lld %lld %lld %lld %lld", &d, &F, &swiglu, &groups, &rows_max, &rr_R, &rr_L) != 7)
-    fail("input: d F swiglu groups rows_max rr_R rr_L offsets...");
+    fail("input: d F swiglu groups rows_max rr_R rr_L offsets... [chunks, then chunks+1 rows of groups bounds]");
   std::vector<int64_t> off(groups + 1);
   for (auto& o : off)
     if (std::scanf("%lld", (long long*)&o) != 1) fail("input: offsets");
   if (off[0] != 0 || off[groups] > rows_max) fail("input: offsets");
   for (int g = 0; g < groups; ++g)
     if (off[g + 1] < off[g]) fail("input: offsets must ascend");
+  // optional token chunks: bounds[r][g] = first row of chunk r in group g
+  // (bounds[0] = the group starts, bounds[chunks] = the group ends); the
+  // row-split launches then also run once per chunk on [bounds[r], bounds[r+1])
+  long long chunks = 0;
+  std::vector<std::vector<int64_t>> bounds;
+  if (std::scanf("%lld", &chunks) == 1) {
+    bounds.assign(chunks + 1, std::vector<int64_t>(groups));
+    for (auto& row : bounds)
+      for (auto& b : row)
+        if (std::scanf("%lld", (long long*)&b) != 1) fail("input: chunk bounds");
+    for (int g = 0; g < groups; ++g) {
+      if (bounds[0][g] != off[g] || bounds[chunks][g] != off[g + 1]) fail("input: chunk bounds must span the groups");
+      for (int r = 0; r < chunks; ++r)
+        if (bounds[r + 1][g] < bounds[r][g]) fail("input: chunk bounds must ascend");
+    }
+  }
   const int64_t m = swiglu ? 2 : 1;
   if (d * 2 > kMaxRowBytes || m * F * 2 > kMaxRowBytes) fail("input: rows wider than the host limit");
   const int W = (int)groups;  // weight sets (one per group)
   const Tensor x{"x_rows", rows_max * d * 2}, h{"h", rows_max * F * 2}, dy{"dy_rows", rows_max * d * 2},
       dact{"d_act", rows_max * m * F * 2}, w_in{"w_in", W * d * F * 2}, w_up{"w_up", W * d * F * 2},
       w_out{"w_out", W * F * d * 2};
-  // forward: [x] [W_in | W_up] with the activation, then h W_out
-  check_rows({"fwd gate|up", false, swiglu != 0, x, w_in, swiglu ? w_up : w_in, d, F, d * F, F, d, 0}, off,
-             (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
-  check_rows({"fwd down", false, false, h, w_out, w_out, F, d, F * d, d, F, 0}, off, (int)groups, rows_max, (int)rr_R,
-             (int)rr_L, W);
-  // backward: dH = dY W_out^T (activation backward in the epilogue), dx = d_act [W_in | W_up]^T
-  check_rows({"dgrad W_out", true, false, dy, w_out, w_out, d, d, F * d, F, d, 0}, off, (int)groups, rows_max,
-             (int)rr_R, (int)rr_L, W);
   const int64_t b_split = swiglu ? F : 0;
-  if (b_split % BK == 0)  // otherwise the register-staged kernels take this launch
-    check_rows({"dgrad W_in", true, false, dact, w_in, swiglu ? w_up : w_in, m * F, F, d * F, d, m * F, b_split},
-               off, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
+  for (long long r = -1; r < chunks; ++r) {  // r = -1: whole groups; else chunk r's sub-ranges
+    std::vector<int64_t> o = off;
+    const int64_t* ends = nullptr;
+    if (r >= 0) {
+      for (int g = 0; g < groups; ++g) o[g] = bounds[r][g];
+      ends = bounds[r + 1].data();
+    }
+    // forward: [x] [W_in | W_up] with the activation, then h W_out
+    check_rows({"fwd gate|up", false, swiglu != 0, x, w_in, swiglu ? w_up : w_in, d, F, d * F, F, d, 0}, o, ends,
+               (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
+    check_rows({"fwd down", false, false, h, w_out, w_out, F, d, F * d, d, F, 0}, o, ends, (int)groups, rows_max,
+               (int)rr_R, (int)rr_L, W);
+    // backward: dH = dY W_out^T (activation backward in the epilogue), dx = d_act [W_in | W_up]^T
+    check_rows({"dgrad W_out", true, false, dy, w_out, w_out, d, d, F * d, F, d, 0}, o, ends, (int)groups, rows_max,
+               (int)rr_R, (int)rr_L, W);
+    if (b_split % BK == 0)  // otherwise the register-staged kernels take this launch
+      check_rows({"dgrad W_in", true, false, dact, w_in, swiglu ? w_up : w_in, m * F, F, d * F, d, m * F, b_split},
+                 o, ends, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
+  }
   // weight gradients: dW_out = h^T dY, [dW_in | dW_up] = x^T d_act
   check_wgrad({"wgrad W_out", h, dy, F, d, F, d, wgrad_ksplit(groups, F, d, rows_max)}, off, (int)groups);
   check_wgrad({"wgrad W_in", x, dact, d, m * F, d, m * F, wgrad_ksplit(groups, d, m * F, rows_max)}, off,

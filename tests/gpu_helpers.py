@@ -123,13 +123,16 @@ def check_routing(wl, layer, ref, n_check_xperm_bits=True, x_bits=None):
     return n
 
 
-def run_full_parity(wl, inp, dot_floor=False):
+def run_full_parity(wl, inp, dot_floor=False, pipeline_chunks=0):
     """Run one fwd+bwd step on the GPU and compare every output with the
     oracle, element by element.  d_topk_w is held to the plain normwise bar
     unless dot_floor is set (named tiny fuzz cases only, see
-    assert_dot_close)."""
+    assert_dot_close).  pipeline_chunks > 0 runs the pipelined step."""
     layer, w, x, dy = make_layer(wl, inp)
-    layer.step(x, dy, w)
+    if pipeline_chunks:
+        layer.step_pipelined(x, dy, w, chunks=pipeline_chunks)
+    else:
+        layer.step(x, dy, w)
     torch.cuda.synchronize()
     g_logits = host(layer.logits)
     ref = oracle.layer_from_inputs(inp, logits=g_logits)

@@ -47,9 +47,11 @@ def checker():
     return exe
 
 
-def run(exe, d, F, swiglu, offsets, rows_max, rr_R=0, rr_L=1):
+def run(exe, d, F, swiglu, offsets, rows_max, rr_R=0, rr_L=1, bounds=None):
     groups = len(offsets) - 1
     text = f"{d} {F} {int(swiglu)} {groups} {rows_max} {rr_R} {rr_L}\n" + " ".join(map(str, offsets)) + "\n"
+    if bounds is not None:
+        text += f"{len(bounds) - 1}\n" + "\n".join(" ".join(map(str, row)) for row in bounds) + "\n"
     r = subprocess.run([exe], input=text, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0 and r.stdout.startswith("OK"), r.stdout + r.stderr
     return int(r.stdout.split()[1])
@@ -92,6 +94,32 @@ def test_every_gemm_load_stays_in_bounds(checker, name):
     c = CASES[name]
     n = run(checker, c["d"], c["F"], c["swiglu"], offsets_of(c["counts"]), c["rows_max"], c.get("rr_R", 0),
             c.get("rr_L", 1))
+    assert n > 0
+
+
+def chunk_bounds(offsets, chunks, seed):
+    """Random token-chunk sub-ranges of every group: ascending cut points
+    inside each group, some chunks empty."""
+    rng = np.random.default_rng(seed)
+    G = len(offsets) - 1
+    rows = [[offsets[g] for g in range(G)]]
+    cuts = [sorted(rng.integers(offsets[g], offsets[g + 1] + 1, chunks - 1)) for g in range(G)]
+    for r in range(chunks - 1):
+        rows.append([int(cuts[g][r]) for g in range(G)])
+    rows.append([offsets[g + 1] for g in range(G)])
+    return rows
+
+
+@pytest.mark.parametrize("name,chunks", [("dsv2lite_routed_rr", 4), ("mixtral_routed", 2), ("edges", 3),
+                                         ("bertl_skew", 3)])
+def test_gemm_loads_of_token_chunks_stay_in_bounds(checker, name, chunks):
+    """The row-split launches of a pipelined step run once per token chunk on
+    sub-range group tables (offsets = chunk starts, ends = next chunk's
+    starts): every load of every chunk's launches is checked as above."""
+    c = CASES[name]
+    off = offsets_of(c["counts"])
+    n = run(checker, c["d"], c["F"], c["swiglu"], off, c["rows_max"], c.get("rr_R", 0), c.get("rr_L", 1),
+            bounds=chunk_bounds(off, chunks, 7 + chunks))
     assert n > 0
 
 
