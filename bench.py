@@ -137,6 +137,8 @@ def main():
                     help="time replays of the whole step captured in one HIP graph instead of eager calls")
     ap.add_argument("--pipeline", type=int, default=0, metavar="CHUNKS",
                     help="time the step with the batch cut into CHUNKS token chunks on two streams")
+    ap.add_argument("--fused", action="store_true",
+                    help="also time the forward pass alone, unfused and fused (gather prologue, weighted epilogue)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
@@ -274,6 +276,27 @@ def main():
         log(f"[bench] cpu baseline on {args.cpu_tokens} tokens")
         cpu = cpu_baseline(wl, inp, args.cpu_tokens)
 
+    fused = None
+    if args.fused:
+        # forward only: forward() (dispatch copy, saved activations, weighted
+        # combine) against forward_fused() (gather prologue, h only, weighted
+        # un-permuted rows, k-row sum); alternating blocks of steps
+        fwd = {"unfused": lambda: layer.forward(x, w), "fused": lambda: layer.forward_fused(x, w)}
+        samples = {k_: [] for k_ in fwd}
+        for fn in fwd.values():
+            fn()
+        for _ in range(3):
+            for key, fn in fwd.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                for _ in range(args.steps):
+                    fn()
+                b.record(st)
+                torch.cuda.synchronize()
+                samples[key].append(a.elapsed_time(b) / args.steps)
+        fused = {k_ + "_ms": round(float(np.median(v)), 4) for k_, v in samples.items()}
+        fused["tokens_per_s_fused"] = round(wl.T / (fused["fused_ms"] * 1e-3), 1)
+
     pipeline = None
     if args.pipeline:
         # the pages' overlap model (tutorial, 通信优化方法 三): total = T_A +
@@ -306,6 +329,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "pipeline": pipeline,
+        "fused_forward": fused,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(result), flush=True)

@@ -226,6 +226,37 @@ int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,
                        const void* w_out, void* act_saved, void* h,
                        void* y_rows, void* stream);
 
+/* Fused forward of the routed experts (tutorial: 用于分布式 MoE 的主流框架与库
+ * 二, Tutel's fused kernels: gate, routing, expert compute and combine
+ * merged to cut launches and traffic).  For a forward-only pass:
+ *   - GEMM-1 reads each row's activation straight from the token rows,
+ *     x[assign_of_row[r] / k], so the dispatch copy (moe_dispatch with x_perm
+ *     NULL) is not needed, and writes only h (no saved A | B or Z);
+ *   - GEMM-2 writes row r's output, scaled by its gate weight
+ *     topk_w[assign_of_row[r]], to row assign_of_row[r] = t*k + j of y_tok
+ *     [T*k, d]: the un-permuted, weighted rows that moe_combine_fused sums.
+ * The backward needs the unweighted y_perm (for d_topk_w) and x_perm (for
+ * the weight gradients), so training uses moe_expert_ffn_fwd.
+ *   grp: the routed table (groups = E, use_placement, no ends);
+ *   x [T, d], assign_of_row [n_max], topk_w [T, k] (moe_route's,
+ *   moe_dispatch's); h [rows_max, ffn]; y_tok [T*k, d] (rows of dropped
+ *   assignments untouched).
+ * Errors: MOE_ERR_INVALID for a null or misaligned pointer or another group
+ * table, MOE_ERR_UNSUPPORTED for fp32 or T*d*2 > 0x7FFF0000 bytes. */
+int moe_expert_ffn_fwd_fused(const moe_config* cfg, const moe_groups* grp,
+                             const void* x, const int32_t* assign_of_row,
+                             const float* topk_w, const void* w_in,
+                             const void* w_up, const void* w_out, void* h,
+                             void* y_tok, void* stream);
+
+/* Combine of moe_expert_ffn_fwd_fused's weighted token-major rows:
+ *   y[t] = sum over kept j (row_of[t*k+j] >= 0) of y_tok[t*k+j]
+ *          (+ y_shared[t] if not NULL), fp32 accumulation in j order.
+ * Errors: MOE_ERR_INVALID for a null or misaligned pointer. */
+int moe_combine_fused(const moe_config* cfg, const void* y_tok,
+                      const int32_t* row_of, const void* y_shared, void* y,
+                      void* stream);
+
 /* The two halves of moe_expert_ffn_bwd, for callers that pipeline token
  * chunks: moe_expert_ffn_bwd_data computes dL/d act (into ws) and dx_rows for
  * the group table's rows (sub-ranges allowed: grp->ends), and

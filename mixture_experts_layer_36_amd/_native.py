@@ -54,6 +54,8 @@ SIGNATURES = {
     "moe_expert_ffn_bwd_data": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_ffn_bwd_weights": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_permute": [_CFG, _P, _P, _P, _P],
+    "moe_expert_ffn_fwd_fused": [_CFG, _GRP, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_combine_fused": [_CFG, _P, _P, _P, _P, _P],
     "moe_chunk_rows": [_CFG, _P, _P, _P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), _P, _P],
     "moe_combine": [_CFG, _P, _P, _P, _P, _P, _P],
     "moe_combine_bwd": [_CFG, _P, _P, _P, _P, _P, _P, _P],

@@ -77,6 +77,16 @@ def moe_expert_ffn_bwd_weights(cfg, grp, x_rows, h, dy_rows, dw_in, dw_up, dw_ou
          _ptr(dy_rows), _ptr(dw_in), _ptr(dw_up), _ptr(dw_out), _ptr(ws), _stream(stream))
 
 
+def moe_expert_ffn_fwd_fused(cfg, grp, x, assign_of_row, topk_w, w_in, w_up, w_out, h, y_tok, stream=None):
+    call("moe_expert_ffn_fwd_fused", ctypes.byref(cfg), ctypes.byref(grp), _ptr(x), _ptr(assign_of_row),
+         _ptr(topk_w), _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(h), _ptr(y_tok), _stream(stream))
+
+
+def moe_combine_fused(cfg, y_tok, row_of, y_shared, y, stream=None):
+    call("moe_combine_fused", ctypes.byref(cfg), _ptr(y_tok), _ptr(row_of), _ptr(y_shared), _ptr(y),
+         _stream(stream))
+
+
 def moe_permute(cfg, x, row_of, x_perm, stream=None):
     call("moe_permute", ctypes.byref(cfg), _ptr(x), _ptr(row_of), _ptr(x_perm), _stream(stream))
 

@@ -25,7 +25,9 @@ inline int row_unroll(int64_t d, int elem_bytes, int kmax) {
   return nch > 256 ? 8 : nch > 128 ? 4 : 2;
 }
 
-// y[t] = sum_j g[t,j] * y_perm[row_of[t,j]] (+ y_shared[t])
+// y[t] = sum_j g[t,j] * y_perm[row_of[t,j]] (+ y_shared[t]).  With topk_w
+// NULL the rows are already weighted and token-major (the fused forward's
+// GEMM epilogue wrote row t*k + j): y[t] = sum over kept j of y_perm[t*k + j].
 template <typename T, int KMAX, int U>
 __global__ __launch_bounds__(64 * kRowWaves) void combine_kernel(const T* __restrict__ y_perm,
                                                                  const int32_t* __restrict__ row_of,
@@ -39,10 +41,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void combine_kernel(const T* __rest
   const int nch = d / V;
   int rows[KMAX];
   float g[KMAX];
+  const bool tok_major = topk_w == nullptr;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     rows[j] = j < k ? row_of[t * k + j] : -1;
-    g[j] = rows[j] >= 0 ? topk_w[t * k + j] : 0.0f;
+    g[j] = rows[j] >= 0 ? (tok_major ? 1.0f : topk_w[t * k + j]) : 0.0f;
+    if (tok_major && rows[j] >= 0) rows[j] = (int)(t * k + j);
   }
   for (int c0 = lane; c0 < nch; c0 += 64 * U) {
     u32x4 v[KMAX][U], sh[U];

@@ -13,7 +13,11 @@ enum {
   EPI_SWIGLU_FWD = 2,    // tile pairs gate|up columns: C[:, f] = A, C[:, c_split+f] = B, C2 = silu(A)*B
   EPI_GELU_BWD = 3,      // C = acc * GELU'(X1)
   EPI_SWIGLU_BWD = 4,    // X1 = [A|B]; C[:, f] = dA, C[:, c_split+f] = dB with dH = acc
-  EPI_STORE_SPLITN = 5   // wgrad: columns >= c_split go to C2
+  EPI_STORE_SPLITN = 5,  // wgrad: columns >= c_split go to C2
+  // fused forward (no saved activations; weighted, un-permuted output rows)
+  EPI_STORE_SCATTER = 6, // C row scatter[r] = row_scale[scatter[r]] * acc of row r
+  EPI_SWIGLU_FWD_H = 7,  // as EPI_SWIGLU_FWD, writing only C2 = silu(A)*B
+  EPI_GELU_FWD_H = 8     // as EPI_GELU_FWD, writing only C2 = GELU(Z)
 };
 
 struct Args {
@@ -34,6 +38,14 @@ struct Args {
   int rr_R = 0, rr_L = 1;   // round-robin slot -> expert map (rr_R = 0: identity)
   int tiles_m = 0, tiles_n = 0;
   int gm = 8;               // row tiles per ordering group (L2 reuse of column panels)
+  // Row-split A gathered (bf16 direct-load kernels): row r of the group is
+  // row gather[r] / gather_k of A, which has gather_rows rows
+  const int32_t* gather = nullptr;
+  int gather_k = 1;
+  int64_t gather_rows = 0;
+  // EPI_STORE_SCATTER: output row of row r and its scale index
+  const int32_t* scatter = nullptr;
+  const float* row_scale = nullptr;
   // WGRAD split over the reduction (bf16 only): ksplit > 1 launches write
   // fp32 partials [ksplit][weight sets][M][N] to `partial`, then summed
   float* partial = nullptr;

@@ -152,6 +152,23 @@ struct Loader {
       colok[i] = true;
     }
   }
+  // KC gathered: tile row r of the group (r < rows_valid) is row
+  // gather[row_begin + r] / gather_k of the operand; lanes of rows past the
+  // group are masked through their K column (gemm_addr::kc_gather_col).
+  __device__ __forceinline__ void init_kc_gather(int64_t ld, const int32_t* gather, int gather_k, int64_t row_begin,
+                                                 int64_t rows_valid) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - W0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int row, col;
+      kc_lane<BK, NW>(i, wave, lane, row, col);
+      const int32_t a = row < rows_valid ? gather[row_begin + row] : 0;
+      kcol[i] = gemm_addr::kc_gather_col(row, col, rows_valid);
+      voff[i] = (uint32_t)((gemm_addr::gather_token(a, gather_k) * ld + col) * 2);
+      krow[i] = 0;
+      colok[i] = true;
+    }
+  }
   // MN: element (k0 + k, col) of a stage at k * ld + col elements from the
   // base of the stage's resource of the column's panel (col relative to that
   // base, k within the stage).
@@ -366,13 +383,20 @@ struct StagedTile {
 
 // Row-split kernels: EPI_STORE (C), EPI_GELU_FWD (C = Z | C2 = GELU(Z)) and the
 // SwiGLU gate|up pair (C = A | B at column f and c_split + f, C2 = silu(A) B).
+// Variants of the fused forward: EPI_SWIGLU_FWD_H and EPI_GELU_FWD_H write
+// only the hidden activation (C2), EPI_STORE_SCATTER writes output row r to
+// row scatter[r] of C, scaled by row_scale[scatter[r]] before rounding.
 template <int FM, int FN, bool PAIR, int EPI>
 __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc)[FM][FN], const int (&bcol)[FN],
                                                      int wave, int lane, int64_t row_begin, int64_t row_end,
                                                      int64_t n0, int64_t N, char* smem) {
   static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
-  constexpr bool GELU = EPI == gemm::EPI_GELU_FWD;
-  constexpr int SC = PAIR ? 384 : (GELU ? 512 : 256);  // PAIR: A | B | H; GELU: Z | GELU(Z)
+  constexpr bool GELU = EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_GELU_FWD_H;
+  constexpr bool SAVE = EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD;  // also Z or A | B
+  constexpr bool SCAT = EPI == gemm::EPI_STORE_SCATTER;
+  // staged columns: PAIR A | B | H or H; GELU Z | GELU(Z) or GELU(Z); else the output
+  constexpr int SC = PAIR ? (SAVE ? 384 : 128) : (GELU && SAVE ? 512 : 256);
+  constexpr int HOFF = PAIR ? (SAVE ? 256 : 0) : (SAVE ? 256 : 0);  // column of the hidden activation
   const StagedTile<bf16, SC> st{(lds_char*)smem};
   bf16* C = reinterpret_cast<bf16*>(a.C);
   bf16* C2 = reinterpret_cast<bf16*>(a.C2);
@@ -380,6 +404,11 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
   const int sr = 32 * wm + (lane & 31);  // this lane's staged row
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    float scale = 1.0f;
+    if constexpr (SCAT) {  // this lane's row's weight
+      const int64_t rr = row_begin + wm * 128 + 32 * i + (lane & 31);
+      scale = rr < row_end ? a.row_scale[a.scatter[rr]] : 0.0f;
+    }
     __syncthreads();  // the table's previous pass has been stored (and the K ring is idle)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -392,21 +421,23 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
           bv[q] = acc[i][1][4 * g + q];
           hv[q] = av[q] * sigmoid_f(av[q]) * bv[q];
         }
-        st.put4(sr, bcol[0] + tc, av);
-        st.put4(sr, bcol[1] + tc, bv);
-        st.put4(sr, 256 + bcol[0] + tc, hv);
+        if constexpr (SAVE) {
+          st.put4(sr, bcol[0] + tc, av);
+          st.put4(sr, bcol[1] + tc, bv);
+        }
+        st.put4(sr, HOFF + bcol[0] + tc, hv);
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
-          st.put4(sr, bcol[j] + tc, v);
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * scale;
+          if constexpr (!GELU || SAVE) st.put4(sr, bcol[j] + tc, v);
           if constexpr (GELU) {
             float h[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
-            st.put4(sr, 256 + bcol[j] + tc, h);
+            st.put4(sr, HOFF + bcol[j] + tc, h);
           }
         }
       }
@@ -416,7 +447,7 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
       const int64_t rr = row_begin + (r >> 5) * 128 + 32 * i + (r & 31);
       if (rr >= row_end) return;
       if constexpr (PAIR) {
-        const int part = col >> 7, c = col & 127;  // 0: A, 1: B, 2: H
+        const int part = SAVE ? col >> 7 : 2, c = col & 127;  // 0: A, 1: B, 2: H
         if (n0 + c >= N) return;
         if (part == 0) st16(C + rr * a.ldc + n0 + c, v);
         else if (part == 1) st16(C + rr * a.ldc + a.c_split + n0 + c, v);
@@ -424,7 +455,8 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
       } else {
         const int c = col & 255;
         if (n0 + c >= N) return;
-        if (GELU && col >= 256) st16(C2 + rr * a.ldc2 + n0 + c, v);
+        if (GELU && (!SAVE || col >= 256)) st16(C2 + rr * a.ldc2 + n0 + c, v);
+        else if (SCAT) st16(C + (int64_t)a.scatter[rr] * a.ldc + n0 + c, v);
         else st16(C + rr * a.ldc + n0 + c, v);
       }
     });
@@ -565,7 +597,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   constexpr int NC = WM * WN;                 // waves: every wave loads and multiplies
   constexpr int NW = NC, W0 = 0;
   constexpr int FM = BM / (32 * WM), FN = BN / (32 * WN);
-  constexpr bool PAIR = (EPI == gemm::EPI_SWIGLU_FWD);
+  constexpr bool PAIR = (EPI == gemm::EPI_SWIGLU_FWD || EPI == gemm::EPI_SWIGLU_FWD_H);
   constexpr bool BKC = (KIND == gemm::KIND_DGRAD);
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -588,7 +620,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   // A: the tile's rows (at most BM); DGRAD B: the tile's BN weight rows
   // (K-contiguous); FWD B (N-contiguous): rebased at every K stage in issue.
   BufRes ra, rb0, rb1;
-  ra.init(Ab, gemm_addr::rows_a_span(row_begin, rows_valid, a.lda));
+  if (a.gather) ra.init(Ab, gemm_addr::gather_a_span(a.gather_rows, a.lda));
+  else ra.init(Ab, gemm_addr::rows_a_span(row_begin, rows_valid, a.lda));
   if (KIND == gemm::KIND_DGRAD) {
     rb0.init(Bg, gemm_addr::dgrad_b_span(0, n0, BN, N, a.ldb));
     rb1.init(B2g, gemm_addr::dgrad_b_span(0, n0, BN, N, a.ldb));
@@ -597,7 +630,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Loader<BM, BK, true, NW, W0> la;
   Loader<BN, BK, BKC, NW, W0> lb;
-  la.init_kc(a.lda);
+  if (a.gather) la.init_kc_gather(a.lda, a.gather, a.gather_k, row_begin, rows_valid);
+  else la.init_kc(a.lda);
   if constexpr (BKC) lb.init_kc(a.ldb);
   else lb.init_mn(a.ldb, PAIR, N - n0);
   const bool split = BKC && a.b_split > 0;
@@ -658,7 +692,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm3_rows_kernel(Args a) {
       [&]() { mma_frags<FM, FN, BK>(fr, acc); });
 
   if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
-                (EPI == gemm::EPI_STORE || EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD))
+                (EPI == gemm::EPI_STORE || EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD ||
+                 EPI == gemm::EPI_STORE_SCATTER || EPI == gemm::EPI_GELU_FWD_H || EPI == gemm::EPI_SWIGLU_FWD_H))
     rows_epilogue_staged<FM, FN, PAIR, EPI>(a, acc, bcol, wave, lane, row_begin, row_end, n0, N, smem);
   else if constexpr (NP == kPingPong && BM == 256 && BN == 256 && WM == 2 && WN == 4 &&
                      (EPI == gemm::EPI_GELU_BWD || EPI == gemm::EPI_SWIGLU_BWD))
@@ -873,7 +908,8 @@ __global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(Args a, int epi
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS, int NP, int KIND, int EPI>
 hipError_t launch_rows(Args a, int64_t rows_max, hipStream_t st) {
-  gemm_addr::rows_tiles(a.N, EPI == gemm::EPI_SWIGLU_FWD ? BN / 2 : BN, rows_max, a.groups, BM, a.tiles_m, a.tiles_n);
+  constexpr bool PAIR = EPI == gemm::EPI_SWIGLU_FWD || EPI == gemm::EPI_SWIGLU_FWD_H;
+  gemm_addr::rows_tiles(a.N, PAIR ? BN / 2 : BN, rows_max, a.groups, BM, a.tiles_m, a.tiles_n);
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -917,6 +953,9 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
       case EPI_STORE: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_STORE>(a, rows_max, st);
       case EPI_GELU_FWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_GELU_FWD>(a, rows_max, st);
       case EPI_SWIGLU_FWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_SWIGLU_FWD>(a, rows_max, st);
+      case EPI_STORE_SCATTER: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_STORE_SCATTER>(a, rows_max, st);
+      case EPI_GELU_FWD_H: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_GELU_FWD_H>(a, rows_max, st);
+      case EPI_SWIGLU_FWD_H: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_SWIGLU_FWD_H>(a, rows_max, st);
     }
   } else {
     switch (epi) {

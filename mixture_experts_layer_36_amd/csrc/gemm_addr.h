@@ -208,6 +208,15 @@ MOE_HD Span dgrad_b_span(int64_t set_base, int64_t n0, int64_t nrows_max, int64_
   return Span{set_base + n0 * ldb * 2, min64(nrows_max, N - n0) * ldb * 2};
 }
 
+// Row-split A gathered from the token rows (the fused forward): tile row r
+// of the group is token row gather[row_begin + r] / gather_k of x, whose
+// resource spans all x_rows rows; a lane whose tile row is past the group's
+// rows is masked by a K offset no stage reaches (kc_gather_col).
+MOE_HD Span gather_a_span(int64_t x_rows, int64_t lda) { return Span{0, x_rows * lda * 2}; }
+constexpr int kMaskedCol = 1 << 30;
+MOE_HD int kc_gather_col(int row, int col, int64_t rows_valid) { return row < rows_valid ? col : kMaskedCol; }
+MOE_HD int64_t gather_token(int32_t assign, int gather_k) { return (int64_t)assign / gather_k; }
+
 // A stage of an M/N-contiguous operand whose K row k starts at first +
 // k * ld_bytes (first points at the tile's first column, col0_bytes into its
 // row): stage kt covers K rows [kt BK, kt BK + BK).  Every stage has the same

@@ -175,6 +175,34 @@ hipError_t ffn_fwd(const moe_config* c, const moe_groups* g, const void* x, cons
 }
 
 // Data gradients: dL/d act into ws (rows as in the row buffers), then dx.
+// The fused forward (bf16): GEMM-1 reads its rows from the token rows
+// through assign_of_row, writes only h; GEMM-2 writes row r to row
+// assign_of_row[r] of y_tok scaled by topk_w there.
+hipError_t ffn_fwd_fused(const moe_config* c, const moe_groups* g, const void* x, const int32_t* assign_of_row,
+                         const float* topk_w, const void* w_in, const void* w_up, const void* w_out, void* h,
+                         void* y_tok, hipStream_t st) {
+  using namespace moe::gemm;
+  const int64_t d = c->d, F = g->ffn;
+  const bool swiglu = c->act == MOE_ACT_SWIGLU;
+  Args a1;
+  fill_placement(c, g, a1);
+  a1.A = x; a1.lda = d;
+  a1.gather = assign_of_row; a1.gather_k = (int)c->k; a1.gather_rows = c->T;
+  a1.B = w_in; a1.B2 = swiglu ? w_up : nullptr; a1.ldb = F; a1.b_gstride = d * F;
+  a1.N = F; a1.K = d;
+  a1.C2 = h; a1.ldc2 = F;
+  hipError_t e = run_rows<moe::bf16>(KIND_FWD, swiglu ? EPI_SWIGLU_FWD_H : EPI_GELU_FWD_H, a1, g->rows_max, st);
+  if (e != hipSuccess) return e;
+  Args a2;
+  fill_placement(c, g, a2);
+  a2.A = h; a2.lda = F;
+  a2.B = w_out; a2.ldb = d; a2.b_gstride = F * d;
+  a2.N = d; a2.K = F;
+  a2.C = y_tok; a2.ldc = d;
+  a2.scatter = assign_of_row; a2.row_scale = topk_w;
+  return run_rows<moe::bf16>(KIND_FWD, EPI_STORE_SCATTER, a2, g->rows_max, st);
+}
+
 template <typename T>
 hipError_t ffn_bwd_data(const moe_config* c, const moe_groups* g, const void* w_in, const void* w_up,
                         const void* w_out, const void* act_saved, const void* dy, void* dx, void* ws, hipStream_t st) {
@@ -457,6 +485,38 @@ int moe_expert_ffn_bwd(const moe_config* cfg, const moe_groups* grp, const void*
                      : ffn_bwd<float>(cfg, grp, x_rows, w_in, w_up, w_out, act_saved, h, dy_rows, dx_rows, dw_in,
                                       dw_up, dw_out, ws, st);
   return hip_status(e);
+}
+
+int moe_expert_ffn_fwd_fused(const moe_config* cfg, const moe_groups* grp, const void* x, const int32_t* assign_of_row,
+                             const float* topk_w, const void* w_in, const void* w_up, const void* w_out, void* h,
+                             void* y_tok, void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  s = check_groups(cfg, grp);
+  if (s != MOE_OK) return s;
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  if (!x || !assign_of_row || !topk_w || !w_in || !w_out || !h || !y_tok || (swiglu && !w_up))
+    return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_in) || !aligned16(w_out) || !aligned16(h) || !aligned16(y_tok) ||
+      (swiglu && !aligned16(w_up)))
+    return MOE_ERR_INVALID;
+  if (grp->ends || grp->groups != cfg->E || !grp->use_placement) return MOE_ERR_INVALID;  // the routed table
+  // bf16 direct-load kernels only; x is read through one buffer resource
+  if (cfg->dtype != MOE_BF16 || cfg->T * cfg->d * 2 > moe::gemm_common::kMaxExtent) return MOE_ERR_UNSUPPORTED;
+  return hip_status(ffn_fwd_fused(cfg, grp, x, assign_of_row, topk_w, w_in, w_up, w_out, h, y_tok,
+                                  (hipStream_t)stream));
+}
+
+int moe_combine_fused(const moe_config* cfg, const void* y_tok, const int32_t* row_of, const void* y_shared, void* y,
+                      void* stream) {
+  int s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!y_tok || !row_of || !y) return MOE_ERR_INVALID;
+  if (!aligned16(y_tok) || !aligned16(y) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID;
+  moe::CombineArgs a{};
+  a.y_perm = y_tok; a.row_of = row_of; a.topk_w = nullptr; a.y_shared = y_shared; a.y = y;
+  a.T = cfg->T; a.d = cfg->d; a.k = (int)cfg->k;
+  return hip_status(moe::launch_combine(a, cfg->dtype == MOE_BF16, (hipStream_t)stream));
 }
 
 int moe_expert_ffn_bwd_data(const moe_config* cfg, const moe_groups* grp, const void* w_in, const void* w_up,

@@ -177,6 +177,26 @@ class MoELayer:
         self.forward(x, w)
         self.backward(x, dy, w)
 
+    # ---------------------------------------------------------- fused forward
+    def forward_fused(self, x, w: Weights):
+        """Forward-only pass through the fused path (Tutel's fused kernels in
+        the tutorial's framework section): the layout without the dispatch
+        copy, GEMM-1 gathering its rows from x through assign_of_row and
+        keeping only h, GEMM-2 writing weighted, un-permuted rows, and a
+        plain k-row sum.  y equals forward()'s within rounding (each row is
+        weighted before its bf16 rounding instead of after)."""
+        if getattr(self, "y_tok", None) is None:
+            self.y_tok = torch.empty(self.T * self.k, self.d, dtype=self.dtype, device=self.device)
+        self.route(x, w)
+        api.moe_dispatch(self.cfg, None, self.topk_idx, None, self.row_of, self.assign_of_row, self.raw_counts,
+                         self.expert_counts, self.expert_offsets, self.send_counts, self.send_offsets, self.ws)
+        api.moe_expert_ffn_fwd_fused(self.cfg, self.grp, x, self.assign_of_row, self.topk_w, w.w1, w.w_up, w.w2,
+                                     self.h, self.y_tok)
+        if self.n_shared:
+            self.shared_fwd(x, w)
+        api.moe_combine_fused(self.cfg, self.y_tok, self.row_of, self.y_shared if self.n_shared else None, self.y)
+        return self.y
+
     # ------------------------------------------------------------ pipelined
     def _pipeline_setup(self, chunks):
         """Per-chunk configs (the same layer over a token range, for the

@@ -127,6 +127,9 @@ struct RowsLaunch {
   bool dgrad, pair;
   Tensor A, B, B2;
   int64_t lda, ldb, gstride, N, K, b_split;
+  const int32_t* gather = nullptr;  // the fused forward: A rows gathered from the token rows
+  int gather_k = 1;
+  int64_t gather_rows = 0;
 };
 
 // ends: null (group g owns [off[g], off[g + 1])) or [groups] sub-range ends.
@@ -161,7 +164,7 @@ void check_rows(const RowsLaunch& L, const std::vector<int64_t>& off, const int6
     const int64_t rows_valid = min64(BM, re - rb);
     const int64_t n0 = L.pair ? (int64_t)nt * (BN / 2) : (int64_t)nt * BN;
     const int64_t set0 = (int64_t)wi * L.gstride * 2;
-    const Span sa = rows_a_span(rb, rows_valid, L.lda);
+    const Span sa = L.gather ? gather_a_span(L.gather_rows, L.lda) : rows_a_span(rb, rows_valid, L.lda);
     const StageWalk wb = fwd_b_walk(n0, BK, L.ldb);
     const int nk = (int)((L.K + BK - 1) / BK);
     for (int kt : sample_stages(nk)) {
@@ -171,10 +174,18 @@ void check_rows(const RowsLaunch& L, const std::vector<int64_t>& off, const int6
           for (int i = 0; i < QA; ++i) {  // A: the tile's rows, K-contiguous
             int row, col;
             kc_lane<BK, NW>(i, wave, lane, row, col);
-            const bool ok = k0 + col < L.K;
-            const uint32_t o = ok ? (uint32_t)(((int64_t)row * L.lda + col) * 2) : kOOB;
             const bool valid = row < rows_valid && k0 + col < L.K;
-            const int64_t want = ((rb + row) * L.lda + k0 + col) * 2;
+            uint32_t o;
+            int64_t want;
+            if (L.gather) {  // the lane's token row, masked through its K column past the group
+              const int64_t tok = row < rows_valid ? gather_token(L.gather[rb + row], L.gather_k) : 0;
+              const int kc = kc_gather_col(row, col, rows_valid);
+              o = k0 + kc < L.K ? (uint32_t)((tok * L.lda + col) * 2) : kOOB;
+              want = (tok * L.lda + k0 + col) * 2;
+            } else {
+              o = k0 + col < L.K ? (uint32_t)(((int64_t)row * L.lda + col) * 2) : kOOB;
+              want = ((rb + row) * L.lda + k0 + col) * 2;
+            }
             check_load(L.name, L.A, sa, o, (uint32_t)(k0 * 2), valid, want, (i * NW + wave) * 1024 + lane * 16,
                        A_BYTES);
           }
@@ -320,6 +331,20 @@ int main() {
     if (b_split % BK == 0)  // otherwise the register-staged kernels take this launch
       check_rows({"dgrad W_in", true, false, dact, w_in, swiglu ? w_up : w_in, m * F, F, d * F, d, m * F, b_split},
                  o, ends, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
+  }
+  // the fused forward's GEMM-1: rows gathered from T = rows_max tokens of x
+  // through a synthetic assignment map (t*k + j, k = 2), every row a
+  // different token choice
+  {
+    const int gk = 2;
+    std::vector<int32_t> assign(rows_max);
+    for (int64_t r = 0; r < rows_max; ++r) assign[r] = (int32_t)((r * 2654435761LL) % (rows_max * gk));
+    const Tensor xt{"x (tokens)", rows_max * d * 2};
+    RowsLaunch L{"fused gate|up", false, swiglu != 0, xt, w_in, swiglu ? w_up : w_in, d, F, d * F, F, d, 0};
+    L.gather = assign.data();
+    L.gather_k = gk;
+    L.gather_rows = rows_max;
+    if (rows_max * d * 2 <= kMaxExtent) check_rows(L, off, nullptr, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
   }
   // weight gradients: dW_out = h^T dY, [dW_in | dW_up] = x^T d_act
   check_wgrad({"wgrad W_out", h, dy, F, d, F, d, wgrad_ksplit(groups, F, d, rows_max)}, off, (int)groups);
