@@ -44,7 +44,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-GEMM_SOURCES = ("gemm3.hip", "gemm_common.h", "gemm.h", "common.h", "moe_api.hip")
+GEMM_SOURCES = ("gemm3.hip", "gemm_common.h", "gemm_addr.h", "gemm.h", "common.h", "moe_api.hip")
 
 
 def gemm_source_hash():

@@ -73,6 +73,10 @@ MOE_HD void grouped_order(int lin, int tiles_m, int tiles_n, int& mt, int& nt, i
 MOE_HD int64_t group_end(const int64_t* offsets, const int64_t* ends, int g) {
   return ends ? ends[g] : offsets[g + 1];
 }
+// Tiles are walked group by group (a group's tiles are consecutive linear
+// ids, so an XCD works on few groups' weight panels at a time), and within a
+// group in row bands of at most gm row tiles, balanced (a group of 17 row
+// tiles with gm 8 walks bands of 6, 6 and 5), each band column by column.
 template <int BM>
 MOE_HD bool row_tile_of(const int64_t* offsets, const int64_t* ends, int groups, int tiles_n, int gm, int hw, int& g,
                         int64_t& row_begin, int64_t& row_end, int& nt) {
@@ -80,19 +84,23 @@ MOE_HD bool row_tile_of(const int64_t* offsets, const int64_t* ends, int groups,
   for (int gg = 0; gg < groups; ++gg) real_m += (int)((group_end(offsets, ends, gg) - offsets[gg] + BM - 1) / BM);
   const int real = real_m * tiles_n;
   if (hw >= real) return false;
-  int mt;
-  grouped_order(xcd_remap(hw, real), real_m, tiles_n, mt, nt, gm);
+  const int lin = xcd_remap(hw, real);
   int acc_t = 0;
   for (int gg = 0; gg < groups; ++gg) {
     const int64_t o0 = offsets[gg], o1 = group_end(offsets, ends, gg);
     const int nt_g = (int)((o1 - o0 + BM - 1) / BM);
-    if (mt < acc_t + nt_g) {
+    const int cnt = nt_g * tiles_n;
+    if (lin < acc_t + cnt) {
+      const int bands = (nt_g + gm - 1) / gm;
+      const int band_m = (nt_g + bands - 1) / bands;
+      int mt;
+      grouped_order(lin - acc_t, nt_g, tiles_n, mt, nt, band_m);
       g = gg;
-      row_begin = o0 + (int64_t)(mt - acc_t) * BM;
+      row_begin = o0 + (int64_t)mt * BM;
       row_end = o1;
       return true;
     }
-    acc_t += nt_g;
+    acc_t += cnt;
   }
   return false;
 }
