@@ -139,8 +139,8 @@ int moe_plan(const moe_config* cfg, moe_sizes* out);
  *   index ascending), first k — equal logits go to the lower index.
  *   topk_w [T, k] fp32: gate weights per cfg->gating.
  *   ws: caller workspace of moe_plan's workspace_bytes, 16-byte aligned;
- *   required for bf16 (the call writes a re-packed copy of w_router there),
- *   may be NULL for fp32.
+ *   required for bf16 (the call may write a re-packed copy of w_router
+ *   there: more than 16 experts or d above 4096), may be NULL for fp32.
  * Errors: MOE_ERR_INVALID for a null required pointer or a misaligned x / ws. */
 int moe_route(const moe_config* cfg, const void* x, const void* w_router,
               const float* bias, float* logits, int32_t* topk_idx,

@@ -63,6 +63,18 @@ __device__ __forceinline__ u32x4 pack16<bf16>(const float* in) {
   return v;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane j addresses 4 consecutive 16-bit columns of row j / 4 of a 4 x 16
+// block, and lane i receives column i's 4 values (rows 0..3).  p is an LDS
+// address, 8-byte aligned.
+typedef short i16x4_lds_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) i16x4_lds_t lds_i16x4;
+  const i16x4_lds_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -22,6 +22,9 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace moe {
 
 namespace {
@@ -372,15 +375,465 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_mfma_kernel(
   else finish_token<EP, false>(lv, t, E, k, gating, bias, logits, topk_idx, topk_w);
 }
 
+static hipError_t pack_router_frags(const RouteArgs& a, int NB, hipStream_t st) {
+  const int64_t nfrag = (int64_t)((a.d + 31) / 32) * NB * 64;
+  hipLaunchKernelGGL(pack_router_frags_kernel, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)a.w, (u32x4*)a.wpack, a.d, a.E, NB);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16, up to 16 experts, d up to 4096: the streaming gate GEMM.  Workgroups
+// of 8 waves stay resident and walk "steps" of 16 SG tokens (SG = 8 / WPG
+// groups of 16 tokens): the WPG waves of a group split its K range into
+// contiguous slices of KB 32-K blocks, so every row of a step is read in WPG
+// runs of 64 KB bytes at once, and the workgroup reads its rows whole within
+// one step (DRAM page locality).  Two steps' x operands are in flight per
+// wave: the loads of step i + 2 go out after step i's MFMAs and stay
+// outstanding across the step's barrier, which waits for LDS traffic only.
+// The waves' partial logits meet in LDS; wave i % WPG of a group sums them in
+// the fixed order of the K slices (deterministic logits) and finishes the
+// group's tokens, four lanes per token.
+//
+// Router fragments: the workgroup copies W_r [d][E] into LDS once (rows of
+// `wpitch` bytes) and each wave takes the B operands of its slice from there
+// with transposing reads (ds_read_b64_tr_b16: within 16 lanes, lane j
+// addresses 4 consecutive columns of row j / 4 of a 4 x 16 block and lane i
+// receives column i's 4 rows), keeping them in registers for the kernel.
+// The LDS then holds the partials.
+//
+// With at most 8 experts (PAIRS) a load instruction reads whole 128-byte
+// lines: 8 tokens x 128 bytes.  The MFMA's rows 0..7 then carry the even
+// 16-byte pieces of tokens 0..7 and rows 8..15 their odd pieces; B columns
+// 0..7 hold experts 0..7 at the even pieces' K and columns 8..15 the same
+// experts at the odd pieces' K, so a token's logit is C[t][e] + C[t+8][e+8]
+// (the other two quadrants are unused).  One MFMA still covers 1 KB of x,
+// and the fragments of a 64-K line fill all 16 columns (half the registers).
+// ---------------------------------------------------------------------------
+// value of lane l ^ 1 (XM = 1) or l ^ 2 (XM = 2) within each group of four
+template <int XM>
+__device__ __forceinline__ int quad_xor(int v) {
+  // DPP quad permutations [1, 0, 3, 2] and [2, 3, 0, 1]
+  return __builtin_amdgcn_update_dpp(0, v, XM == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false);
+}
+template <int XM>
+__device__ __forceinline__ float quad_xor(float v) {
+  return __int_as_float(quad_xor<XM>(__float_as_int(v)));
+}
+
+// (value, expert) of the better of two candidates: the larger value, then
+// the lower expert index
+__device__ __forceinline__ void better_of(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+
+// End of routing for 16 tokens spread over a wave, four lanes per token: lane
+// l holds the summed products of token t for experts e0 .. e0 + 3, e0 =
+// 4 (l % 4), and the same bias entries in bq.  The same results as
+// finish_token: bias, logits row, softmax statistics, k rounds of arg-max by
+// (value desc, index asc), gate weights; the statistics are combined across
+// the four lanes with xor shuffles.  Round j's pick is stored by lane j % 4.
+__device__ __forceinline__ void finish_quad(const f32x4& acc, const float (&bq)[4], int64_t t, int64_t Tn, int e0,
+                                            int E, int k, int gating, float* __restrict__ logits,
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  float v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = e0 + c < E ? acc[c] + bq[c] : -INFINITY;
+  const bool live = t < Tn;
+  if (live) {
+    float* lrow = logits + t * E + e0;
+    if ((E & 3) == 0) {
+      if (e0 < E) st16(lrow, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                   __float_as_uint(v[3])});
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e0 + c < E) lrow[c] = v[c];
+    }
+  }
+  // softmax statistics over the token's experts
+  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  mx = fmaxf(mx, quad_xor<1>(mx));
+  mx = fmaxf(mx, quad_xor<2>(mx));
+  float z = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (e0 + c < E) z += __expf(v[c] - mx);
+  z += quad_xor<1>(z);
+  z += quad_xor<2>(z);
+
+  // k rounds of arg-max; every lane of the token sees each round's pick
+  const int part = e0 >> 2;
+  unsigned taken = 0;
+  int my_e[2] = {0, 0};
+  float my_v[2] = {0.0f, 0.0f};
+  float v0 = 0.0f, den = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      float bv = -INFINITY;
+      int be = 1 << 30;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e0 + c < E && !((taken >> c) & 1u) && (be == (1 << 30) || v[c] > bv)) {
+          bv = v[c];
+          be = e0 + c;
+        }
+      better_of(bv, be, quad_xor<1>(bv), quad_xor<1>(be));
+      better_of(bv, be, quad_xor<2>(bv), quad_xor<2>(be));
+      if (be >= e0 && be < e0 + 4) taken |= 1u << (be - e0);
+      if (j == 0) v0 = bv;
+      den += __expf(bv - v0);
+      if ((j & 3) == part) {
+        my_e[j >> 2] = be;
+        my_v[j >> 2] = bv;
+      }
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int j = 4 * r + part;
+    if (j < k) {
+      const float gw = gating == 0 ? __expf(my_v[r] - mx) / z : __expf(my_v[r] - v0) / den;
+      topk_idx[t * k + j] = my_e[r];
+      topk_w[t * k + j] = gw;
+    }
+  }
+}
+
+__device__ __forceinline__ void lds_only_barrier() {
+  // orders LDS traffic only: outstanding global loads stay in flight
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool PAIRS> constexpr int stream_nh() { return PAIRS ? 2 : 1; }  // accumulators per lane
+template <bool PAIRS> constexpr int stream_red_bytes() { return 2 * kMfmaWaves * stream_nh<PAIRS>() * 64 * 16; }
+template <bool PAIRS> constexpr int stream_tab_bytes() { return kMfmaWaves * stream_nh<PAIRS>() * 256 * 4; }
+constexpr int kStreamMaxLds = 4096 * 32;  // W_r rows of up to 16 experts for d = 4096
+
+constexpr int kLdsPerCu = 160 * 1024;
+
+// compute units of the current device (asked once per device)
+static hipError_t device_cus(int* cus) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> count[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int n = count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    count[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
+// bytes per row of W_r in LDS: E bf16, rounded up to 8 bytes (transposing
+// reads take 8-byte aligned addresses)
+static int stream_wpitch(int E) { return (2 * E + 7) / 8 * 8; }
+
+template <int WPG, int KB, bool FULLK, bool PAIRS>
+__global__ __launch_bounds__(kMfmaWaves * 64) void route_stream_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int64_t Tn, int d,
+    int E, int k, int gating, int64_t nsteps, int wpitch) {
+  constexpr int TOKS = 16 * (kMfmaWaves / WPG);
+  constexpr int NH = stream_nh<PAIRS>();
+  constexpr int NW = PAIRS ? KB / 2 : KB;  // router fragments per wave
+  static_assert(KB % 2 == 0, "slices hold an even number of K blocks");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / WPG, kpart = wave % WPG, g = lane >> 4, r16 = lane & 15;
+  const int64_t s0 = blockIdx.x, ds = gridDim.x;
+
+  // (1) W_r: 16-byte chunks of [d][E] in flight before the x loads
+  const int nch = d * E / 8;  // d is a multiple of 8
+  const bool w16 = (reinterpret_cast<uintptr_t>(w) & 15) == 0;  // else 2-byte loads
+  u32x4 wc[16];              // d E <= 65536
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    wc[c] = u32x4{0u, 0u, 0u, 0u};
+    const int ci = tid + 512 * c;
+    if (ci < nch) {
+      if (w16) {
+        wc[c] = ld16(w + 8 * ci);
+      } else {
+        const uint16_t* w2 = reinterpret_cast<const uint16_t*>(w) + 8 * ci;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wc[c][q] = (uint32_t)w2[2 * q] | ((uint32_t)w2[2 * q + 1] << 16);
+      }
+    }
+  }
+
+  // finishing layout: lane l takes token l / 4 of a group, experts e0 .. e0 + 3
+  // (the bias is loaded before the x operands: the waits for W_r cover it)
+  const int e0 = 4 * (lane & 3);
+  float bq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bq[c] = (bias && e0 + c < E) ? bias[e0 + c] : 0.0f;
+
+  // (2) the x operands of the first two steps.  Plain: lane (r, g) reads
+  // token r of its group at K 32 (kb0 + j) + 8 g.  PAIRS: token 8 h + r % 8
+  // at byte 16 (2 g + r / 8) of 128-byte line (line0 + jl), a[2 jl + h].
+  const int kb0 = kpart * KB;
+  const int xoff = PAIRS ? 64 * (kb0 / 2) + 8 * (2 * g + (r16 >> 3)) : 32 * kb0 + 8 * g;  // elements
+  auto load = [&](int64_t s, u32x4 (&a)[KB]) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int64_t t = s * TOKS + 16 * slot + (PAIRS ? 8 * h + (r16 & 7) : r16);
+      const int64_t row = s >= nsteps ? 0 : (t < Tn ? t : Tn - 1);
+      const bf16* xr = x + row * d + xoff;
+#pragma unroll
+      for (int jl = 0; jl < KB / NH; ++jl) {
+        const int step = PAIRS ? 64 : 32;  // elements per load of a lane's row
+        u32x4& dst = a[NH * jl + h];
+        if constexpr (FULLK) {
+          dst = ld16(xr + step * jl);
+        } else if constexpr (PAIRS || KB < 16) {
+          // a piece is all in or all out of d; pieces past it load the row's
+          // first piece (no branch around the load) and are zeroed
+          const bool ok = xoff + step * jl < d;
+          const u32x4 v = ld16(ok ? xr + step * jl : xr - xoff);
+          dst = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          // (16 blocks of 16 experts: a masked load keeps the registers in bounds)
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (xoff + step * jl < d) v = ld16(xr + step * jl);
+          dst = v;
+        }
+      }
+    }
+  };
+  const int64_t iters = s0 < nsteps ? (nsteps - 1 - s0) / ds + 1 : 0;
+  u32x4 xa[KB], xb[KB];
+  load(s0, xa);
+  load(s0 + ds, xb);
+  // (a mask other than the loop's: the loop header must not absorb these
+  // loads as common code of its two predecessors)
+  __builtin_amdgcn_sched_barrier(1);
+
+  // (3) W_r into LDS: element k E + e at byte k wpitch + 2 e
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int ci = tid + 512 * c;
+    if (ci < nch) {
+      if (wpitch == 2 * E) {
+        st16(lds + 16 * ci, wc[c]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int el = 8 * ci + q, kk = el / E, e = el - kk * E;
+          *reinterpret_cast<uint16_t*>(lds + kk * wpitch + 2 * e) = (uint16_t)(wc[c][q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+  }
+  lds_only_barrier();
+
+  // (4) this wave's fragments.  Plain, block kb: lane (n, g) gets K
+  // 32 kb + 8 g .. + 7 of expert n.  PAIRS, line L: lane (n, g) gets K 64 L
+  // + 16 g + 8 (n / 8) .. + 7 of expert n % 8.  Zero past d and past E.
+  u32x4 wb[NW];
+  {
+    const int jr = r16 >> 2, jc = r16 & 3;  // this lane's row and column quad in the 4 x 16 block
+    const int en = PAIRS ? (r16 & 7) : r16;  // expert of the column this lane receives
+#pragma unroll
+    for (int f = 0; f < NW; ++f) {
+      int row, col, kr;  // kr: first K of the piece this lane receives
+      if constexpr (PAIRS) {
+        const int L = kb0 / 2 + f;
+        row = 64 * L + 16 * g + 8 * (jc >> 1) + jr;
+        col = 4 * (jc & 1);
+        kr = 64 * L + 16 * g + 8 * (r16 >> 3);
+      } else {
+        const int kb = kb0 + f;
+        row = 32 * kb + 8 * g + jr;
+        col = 4 * jc;
+        kr = 32 * kb + 8 * g;
+      }
+      const char* pa = lds + (row < d ? row : 0) * wpitch + 2 * col;
+      const u32x2 r0 = lds_read_tr16(pa), r1 = lds_read_tr16(pa + 4 * wpitch);
+      const bool ok = kr < d && en < E;
+      wb[f] = ok ? u32x4{r0[0], r0[1], r1[0], r1[1]} : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  lds_only_barrier();  // the W_r copy is dead: the LDS now holds partials
+
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [2 steps][8 waves][NH][64 lanes]
+  float* tab = reinterpret_cast<float*>(lds + stream_red_bytes<PAIRS>()) + wave * 256 * NH;  // [NH][16][16]
+  // the loads of step i + 2 into a step's operand registers; the other
+  // buffer's loads stay in flight throughout.  The empty asm pins them: their
+  // step index passes through it, and it stays after the barriers and stores
+  // before it.  The scheduling barrier keeps the next MFMAs from moving up.
+  auto reload = [&](int64_t i, u32x4 (&a)[KB]) {
+    int64_t next = s0 + (i + 2) * ds;
+    asm volatile("" : "+s"(next) : : "memory");
+    load(next, a);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto step = [&](int64_t i, u32x4 (&a)[KB]) {
+    f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int j = 0; j < KB; ++j)  // two chains: blocks (plain) or token halves (PAIRS)
+      acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]),
+                                                           __builtin_bit_cast(bf16x8, wb[PAIRS ? j / 2 : j]),
+                                                           acc[j & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sum[NH];
+    if constexpr (PAIRS) {
+      sum[0] = acc[0];
+      sum[NH - 1] = acc[1];
+    } else {
+      sum[0] = acc[0] + acc[1];
+    }
+    const int buf = (int)(i & 1);
+    bool finisher = true;
+    if constexpr (WPG > 1) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) red[((buf * kMfmaWaves + wave) * NH + h) * 64 + lane] = sum[h];
+      lds_only_barrier();
+      finisher = kpart == (int)(i % WPG);
+      if (finisher) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          sum[h] = red[((buf * kMfmaWaves + slot * WPG) * NH + h) * 64 + lane];
+#pragma unroll
+          for (int p = 1; p < WPG; ++p) sum[h] += red[((buf * kMfmaWaves + slot * WPG + p) * NH + h) * 64 + lane];
+        }
+      }
+    }
+    if (finisher) {
+      // accumulator lane l: MFMA rows 4 (l / 16) + q, column l % 16
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tab[(h * 16 + 4 * g + q) * 16 + r16] = sum[h][q];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      const int tt = lane >> 2;  // token of the group
+      f32x4 v4;
+      if constexpr (PAIRS) {
+        // C[t][e] + C[t + 8][e + 8] of half tt / 8 (lanes with e0 >= 8 hold no experts)
+        const float* th = tab + (tt >> 3) * 256 + (tt & 7) * 16;
+        const int e1 = e0 < 8 ? e0 : 0;
+        v4 = *reinterpret_cast<const f32x4*>(th + e1) + *reinterpret_cast<const f32x4*>(th + 8 * 16 + 8 + e1);
+      } else {
+        v4 = *reinterpret_cast<const f32x4*>(tab + tt * 16 + e0);
+      }
+      finish_quad(v4, bq, (s0 + i * ds) * TOKS + 16 * slot + tt, Tn, e0, E, k, gating, logits, topk_idx, topk_w);
+    }
+    // the loads of step i + 2 go out after the finish, which uses their
+    // registers meanwhile (issuing them before the barrier measured slower)
+    reload(i, a);
+  };
+  // both steps in every trip (an odd count gets one more step past the last,
+  // which loads row 0, stores nothing and ends at the same barriers), so that
+  // the loop's back edge always has the other buffer's loads outstanding
+  for (int64_t i = 0; i < iters; i += 2) {
+    step(i, xa);
+    step(i + 1, xb);
+  }
+}
+
+template <int WPG, int KB, bool FULLK, bool PAIRS>
+static hipError_t launch_route_stream_kb(const RouteArgs& a, hipStream_t st) {
+  constexpr int TOKS = 16 * (kMfmaWaves / WPG);
+  const int64_t nsteps = (a.T + TOKS - 1) / TOKS;
+  auto kern = route_stream_kernel<WPG, KB, FULLK, PAIRS>;
+  const int wpitch = stream_wpitch(a.E);
+  const int lds = std::max<int>(a.d * wpitch, stream_red_bytes<PAIRS>() + stream_tab_bytes<PAIRS>());
+  static const hipError_t prep = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kStreamMaxLds);
+  if (prep != hipSuccess) return prep;
+  // resident workgroups: as many as fit on every compute unit at once (the
+  // register-bound count, asked once, capped by this launch's LDS)
+  static int per_cu_regs = 0;
+  static const hipError_t occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu_regs, reinterpret_cast<const void*>(kern), kMfmaWaves * 64,
+      stream_red_bytes<PAIRS>() + stream_tab_bytes<PAIRS>());
+  if (occ != hipSuccess) return occ;
+  int cus = 0;
+  const hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int per_cu = std::max(1, std::min(per_cu_regs, kLdsPerCu / lds));
+  const int64_t grid = std::min<int64_t>(nsteps, (int64_t)cus * per_cu);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMfmaWaves * 64), lds, st, (const bf16*)a.x,
+                     (const bf16*)a.w, a.bias, a.logits, a.topk_idx, a.topk_w, a.T, a.d, a.E, a.k, a.gating,
+                     nsteps, wpitch);
+  return hipGetLastError();
+}
+
+// waves per 16-token group (WPG) and 32-K blocks per wave (KB).  Among the
+// splits whose slices hold at most 16 blocks, prefer one with a step for
+// every compute unit (small T), then one whose slices tile d exactly (no
+// masked pieces), then the fewest waves per group.
+static hipError_t launch_route_stream(const RouteArgs& a, hipStream_t st) {
+  const int nkb = (a.d + 31) / 32;
+  int cus = 0;
+  const hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  int wpg = 0, kb = 0, score = -1;
+  bool full = false;
+  for (int w = 1; w <= kMfmaWaves; w *= 2) {
+    const int need = (nkb + w - 1) / w;
+    if (need > 16) continue;
+    const bool f = a.d == 32 * need * w && (need == 4 || need == 6 || need == 8 || need == 12 || need == 16);
+    const int64_t toks = 16 * (kMfmaWaves / w);
+    const bool wide = (a.T + toks - 1) / toks >= cus;
+    const int sc = (wide ? 2 : 0) + (f ? 1 : 0);
+    if (sc > score) {
+      score = sc;
+      wpg = w;
+      full = f;
+      kb = f ? need : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    }
+  }
+  const bool pairs = a.E <= 8;
+#define MOE_RS(W, K, F)                                                                         \
+  return pairs ? launch_route_stream_kb<W, K, F, true>(a, st) : launch_route_stream_kb<W, K, F, false>(a, st);
+#define MOE_RS_KB(W)                                  \
+  if (full) {                                         \
+    switch (kb) {                                     \
+      case 4: MOE_RS(W, 4, true)                      \
+      case 6: MOE_RS(W, 6, true)                      \
+      case 8: MOE_RS(W, 8, true)                      \
+      case 12: MOE_RS(W, 12, true)                    \
+      default: MOE_RS(W, 16, true)                    \
+    }                                                 \
+  } else {                                            \
+    switch (kb) {                                     \
+      case 4: MOE_RS(W, 4, false)                     \
+      case 8: MOE_RS(W, 8, false)                     \
+      default: MOE_RS(W, 16, false)                   \
+    }                                                 \
+  }
+  switch (wpg) {
+    case 1: MOE_RS_KB(1)
+    case 2: MOE_RS_KB(2)
+    case 4: MOE_RS_KB(4)
+    default: MOE_RS_KB(8)
+  }
+#undef MOE_RS_KB
+#undef MOE_RS
+}
+
 template <int EP, int TG>
 static hipError_t launch_route_mfma(const RouteArgs& a, hipStream_t st) {
   const int64_t blocks = (a.T + 16 * TG - 1) / (16 * TG);
   if (blocks <= 0) return hipSuccess;
   constexpr int NB = EP / 16;
-  const int64_t nfrag = (int64_t)((a.d + 31) / 32) * NB * 64;
-  hipLaunchKernelGGL(pack_router_frags_kernel, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)a.w, (u32x4*)a.wpack, a.d, a.E, NB);
-  hipError_t err = hipGetLastError();
+  hipError_t err = pack_router_frags(a, NB, st);
   if (err != hipSuccess) return err;
   constexpr size_t red = (size_t)(kMfmaWaves / 2) * TG * NB * 4 * 64 * 4;
   constexpr size_t tab = (size_t)16 * TG * EP * 4;
@@ -432,7 +885,9 @@ hipError_t launch_route(const RouteArgs& a, bool bf16_dtype, hipStream_t st) {
     return launch_route_f32<64>(a, st);
   }
   switch (route_mfma_ep(a.E)) {
-    case 16: return launch_route_mfma<16, 2>(a, st);
+    case 16:
+      if (a.d <= 4096 && a.T > 0) return launch_route_stream(a, st);
+      return launch_route_mfma<16, 2>(a, st);
     case 32: return launch_route_mfma<32, 4>(a, st);
     default: return launch_route_mfma<64, 4>(a, st);
   }

@@ -354,14 +354,7 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
 // owns 256 columns (64 per wave) for all experts and tb tokens; the next
 // step's global loads are in flight while the current one is multiplied.
 constexpr int kRwbCols = 256;
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const __attribute__((address_space(3))) char*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
 
 template <int EP>
 __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* __restrict__ x,

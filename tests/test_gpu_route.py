@@ -1,0 +1,144 @@
+"""GPU parity of the bf16 gate (moe_route) against the oracle, through the C
+ABI, over the launch shapes of its kernels.
+
+Up to 16 experts and model widths up to 4096 run the streaming kernel: the
+waves of a 16-token group split its K range into 1, 2, 4 or 8 slices of 4,
+6, 8, 12 or 16 32-K blocks, slices that tile d exactly or end in masked
+pieces; with at most 8 experts a load covers whole 128-byte lines (the
+paired layout); resident workgroups walk the groups two steps at a time (odd
+step counts add one step past the end); the router weights are staged in
+LDS as whole rows or, for expert counts that are not multiples of 4, element
+by element.  The cases below reach these forms (the split each one takes on
+a 256-CU device is named), with ragged T, k from 1 to 8, the three gating
+modes and the router bias.  Wider rows and more experts run the per-block
+kernel.
+
+Bars: logits max|err| / max|ref| <= 1e-5 against the float64 oracle (fp32
+accumulation of bf16 products); the top-k indices equal the oracle's
+selection on the GPU's own logits; gate weights within 1e-6 relative of the
+oracle's on those logits; two runs give bit-identical outputs.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.tensors import normal, zipf_bias
+from mixture_experts_layer_36_amd import _native
+from mixture_experts_layer_36_amd.layer import MoELayer, Weights
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+from gpu_helpers import TOL_LOGITS, bits, dev, host, rel_err  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def native_lib():
+    if not os.path.exists(_native.LIB_PATH):
+        pytest.fail("libmoe.so is not built; build it before running GPU tests")
+    _native.load()
+
+
+# name: (T, d, E, k, gating, bias zipf exponent or None, seed)
+# comments: waves per group x blocks per slice, tiling or masked, paired or not
+CASES = {
+    # 8 x 16, tiling, paired; 769 steps: some workgroups walk an odd count
+    "T12293_d4096_E8": (12293, 4096, 8, 2, "topk_softmax", None, 101),
+    # 8 x 16, masked, paired
+    "T3000_d4000_E8_bias": (3000, 4000, 8, 2, "softmax_topk", 1.2, 102),
+    # 8 x 12, tiling, 16 experts; a single partial step
+    "T65_d3072_E16_k1": (65, 3072, 16, 1, "softmax_topk", None, 103),
+    # 8 x 16, masked, paired: 65 blocks of d = 2056
+    "T513_d2056_E8": (513, 2056, 8, 3, "softmax_topk_renorm", 1.0, 104),
+    # 8 x 16, masked, 16 experts
+    "T300_d2056_E16": (300, 2056, 16, 4, "softmax_topk", None, 114),
+    # 8 x 8, tiling, paired; 5 experts staged element by element
+    "T4099_d2048_E5": (4099, 2048, 5, 3, "softmax_topk_renorm", None, 105),
+    # 8 x 4, tiling, 16 experts with a bias
+    "T5000_d1024_E16_bias": (5000, 1024, 16, 4, "topk_softmax", 1.2, 106),
+    # 2 x 16, tiling, 16 experts (the BERT-large router shape)
+    "T16384_d1024_E16": (16384, 1024, 16, 2, "softmax_topk_renorm", 1.2, 115),
+    # 4 x 6, tiling, paired (the GPT-2 router shape)
+    "T8191_d768_E8": (8191, 768, 8, 2, "softmax_topk_renorm", None, 107),
+    # 2 x 12, tiling, paired; 6 experts staged element by element
+    "T2000_d768_E6": (2000, 768, 6, 2, "topk_softmax", 0.8, 116),
+    # 1 x 16, tiling, 12 experts
+    "T700_d512_E12": (700, 512, 12, 2, "softmax_topk", None, 117),
+    # 1 x 8, masked (7 of 8 blocks in d); k = 8 of 13 experts
+    "T777_d200_E13_k8": (777, 200, 13, 8, "softmax_topk", 0.8, 108),
+    # 1 x 8, tiling, paired; a single expert
+    "T33_d256_E1": (33, 256, 1, 1, "softmax_topk", None, 109),
+    # 1 x 4, masked, paired; one token, one 8-wide piece of d
+    "T1_d8_E2": (1, 8, 2, 2, "topk_softmax", None, 110),
+    # 1 x 4, masked, 16 experts; several steps per workgroup
+    "T200000_d64_E16": (200000, 64, 16, 2, "softmax_topk", None, 111),
+    # wider than 4096: the per-block kernel
+    "T300_d8192_E8": (300, 8192, 8, 2, "softmax_topk", None, 112),
+    # more than 16 experts: the per-block kernel
+    "T500_d1024_E32": (500, 1024, 32, 4, "softmax_topk_renorm", 1.0, 113),
+}
+
+
+def run_route(T, d, E, k, gating, zipf, seed):
+    x = normal(seed * 7 + 1, (T, d), "bf16", 1.0)
+    w_router = normal(seed * 7 + 2, (d, E), "bf16", 0.02)
+    bias = None if zipf is None else np.asarray(zipf_bias(E, zipf), dtype=np.float32)
+    layer = MoELayer(T, d, 16, E, k, 0.0, gating, "gelu", "bf16")
+    w = Weights(w_router=dev(w_router), w1=None, w2=None, w_up=None, bias=dev(bias), ws_gate=None,
+                ws_up=None, ws_down=None)
+    return layer, w, dev(x), x, w_router, bias
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_parity(name):
+    T, d, E, k, gating, zipf, seed = CASES[name]
+    print(f"\n[case] route {name}", flush=True)
+    sys.stdout.flush()
+    layer, w, xd, x, w_router, bias = run_route(T, d, E, k, gating, zipf, seed)
+    layer.route(xd, w)
+    torch.cuda.synchronize()
+    g_logits = host(layer.logits)
+    ref = oracle.gate_logits(oracle.to_f64(x), oracle.to_f64(w_router), bias)
+    e = rel_err(g_logits, ref)
+    assert e <= TOL_LOGITS, f"logits: {e:.3e}"
+
+    idx = oracle.select_topk(g_logits, k)
+    np.testing.assert_array_equal(host(layer.topk_idx).reshape(T, k), idx)
+    gw = oracle.gate_weights(g_logits, idx, gating)
+    got = host(layer.topk_w).reshape(T, k)
+    np.testing.assert_allclose(got, gw, rtol=1e-6, atol=1e-7)
+
+    # deterministic: a second call gives the same bits
+    l1, i1, w1 = bits(layer.logits).copy(), host(layer.topk_idx).copy(), bits(layer.topk_w).copy()
+    layer.logits.fill_(float("nan"))
+    layer.route(xd, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(layer.logits), l1)
+    np.testing.assert_array_equal(host(layer.topk_idx), i1)
+    np.testing.assert_array_equal(bits(layer.topk_w), w1)
+
+
+def test_route_router_weights_at_any_bf16_offset():
+    """W_r two bytes past a 16-byte boundary: the streaming kernel stages it
+    with 2-byte loads and must give the same bits as from an aligned copy."""
+    T, d, E, k, gating, zipf, seed = 3000, 1024, 8, 2, "softmax_topk", None, 120
+    print("\n[case] route unaligned w_router", flush=True)
+    layer, w, xd, x, w_router, bias = run_route(T, d, E, k, gating, zipf, seed)
+    layer.route(xd, w)
+    torch.cuda.synchronize()
+    l_al, i_al, g_al = bits(layer.logits).copy(), host(layer.topk_idx).copy(), bits(layer.topk_w).copy()
+    buf = torch.empty(d * E + 8, dtype=torch.bfloat16, device="cuda")
+    buf[1:1 + d * E].copy_(w.w_router.reshape(-1))
+    w_mis = buf[1:1 + d * E].view(d, E)
+    assert w_mis.data_ptr() % 16 == 2
+    w.w_router = w_mis
+    layer.logits.fill_(float("nan"))
+    layer.route(xd, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(layer.logits), l_al)
+    np.testing.assert_array_equal(host(layer.topk_idx), i_al)
+    np.testing.assert_array_equal(bits(layer.topk_w), g_al)
