@@ -2,7 +2,8 @@
 // every device scores its local tokens with the replicated router g(x);
 // 用于分布式 MoE 的主流框架与库: a top-k gate with k chosen experts).
 //
-// bf16: the gate GEMM runs on MFMA (route_mfma_kernel, below).
+// bf16: the gate GEMM runs on MFMA: route_stream_kernel for up to 16
+// experts and d up to 4096, route_mfma_kernel otherwise (both below).
 //
 // fp32: a workgroup owns 64 tokens, one per lane, and its W waves (16, or 8
 // for more than 16 experts) split the model width: wave w takes the 128-byte
@@ -14,11 +15,12 @@
 // are the same for every lane, so they come in through wave-uniform scalar
 // loads and feed FMAs straight from scalar registers.
 //
-// Both kernels sum their per-wave partial logits in a fixed binary tree
-// through LDS, so the logits are deterministic.  One lane per token then does
-// the softmax statistics and the k rounds of arg-max sequentially, ordering by
-// (logit descending, expert index ascending): equal logits go to the lower
-// index.
+// Every kernel sums its per-wave partial logits in a fixed order through
+// LDS, so the logits are deterministic.  The softmax statistics and the k
+// rounds of arg-max order by (logit descending, expert index ascending):
+// equal logits go to the lower index.  route_stream_kernel spreads a token
+// over four lanes and combines them with quad shuffles; the other kernels
+// give each token one lane.
 #include "common.h"
 #include "kernels.h"
 

@@ -8,11 +8,12 @@
 //   RENORM / TOPK_SOFTMAX: the weights are a softmax over the chosen logits:
 //                          dl[e_j] = g_j * (dg_j - sum_m g_m dg_m), 0 elsewhere
 // router wgrad: dW_r = x^T dl as a deterministic two-stage reduction over
-//   tokens: each block of tokens writes an fp32 partial [d, E] (vector units,
-//   bf16 MFMA or fp32 MFMA by dtype and E), then the partials are summed in
-//   block order (at most 64 blocks).
+//   tokens: each block of tokens writes an fp32 partial [d, E] (bf16 MFMA for
+//   bf16 x, fp32 MFMA for fp32 x), then the partials are summed in block
+//   order (at most 64 blocks).
 #include "common.h"
 #include "kernels.h"
+
 
 namespace moe {
 
@@ -67,99 +68,8 @@ static hipError_t launch_gating_bwd(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// CPT consecutive elements of a row as floats (16, 8, 4 or 2 bytes).
-template <typename T, int CPT>
-__device__ __forceinline__ void load_row_cols(const T* p, float (&v)[CPT]) {
-  if constexpr (CPT * sizeof(T) == 16) {
-    unpack16<T>(ld16(p), v);
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) v[c] = to_f32(p[c]);
-  }
-}
-
-// partial[b][i][e] = sum over tokens t of token block b of x[t, i] * dl[t, e].
-// A lane owns CPT = 64 / EP consecutive columns (all EP experts: 64 fp32
-// accumulators); the 4 waves of a workgroup take consecutive quarters of the
-// block's tokens, 8 tokens per round with their x loads issued first, the
-// tokens' dlogits coming in through wave-uniform scalar loads.  The waves'
-// sums are added in wave order through LDS, so the partials are deterministic.
+// Waves per workgroup of the fp32 MFMA weight-gradient kernel.
 constexpr int kRwgWaves = 4;
-
-template <typename T, int EP, int CPT, bool FULL>
-__global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_partial_kernel(const T* __restrict__ x,
-                                                                              const float* __restrict__ dl,
-                                                                              float* __restrict__ partial,
-                                                                              int64_t Tn, int d, int E, int tw) {
-  static_assert(CPT * EP == 64, "64 accumulators per lane");
-  constexpr int TU = 8;
-  __shared__ float red[kRwgWaves - 1][64][64];  // [wave - 1][accumulator][lane]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i0 = (blockIdx.x * 64 + lane) * CPT;
-  const bool col_ok = i0 < d;  // d is a multiple of 8: a lane's columns are all in or all out
-  const int64_t tbeg = ((int64_t)blockIdx.y * kRwgWaves + wave) * tw;
-  const int64_t tend = tbeg + tw < Tn ? tbeg + tw : Tn;
-  const int Es = FULL ? EP : E;
-  float acc[CPT][EP];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c)
-#pragma unroll
-    for (int e = 0; e < EP; ++e) acc[c][e] = 0.0f;
-  // one token: x[t, i0..] (unconditional load, zeros by select for lanes
-  // past the last column) times the token's dlogits
-  auto token = [&](int64_t t, const float (&xr)[CPT]) {
-    const float* dlt = dl + t * Es;
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      const float lv = (FULL || e < E) ? dlt[e] : 0.0f;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c][e] = fmaf(xr[c], lv, acc[c][e]);
-    }
-    // one token's dlogits at a time in scalar registers (up to 64)
-    if constexpr (EP >= 32) __builtin_amdgcn_sched_barrier(0);
-  };
-  auto load_x = [&](int64_t t, float (&xr)[CPT]) {
-    load_row_cols<T, CPT>(col_ok ? x + t * d + i0 : x, xr);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) xr[c] = col_ok ? xr[c] : 0.0f;
-  };
-  int64_t t = tbeg;
-  // full rounds of TU tokens: all TU loads issued before the FMAs
-  for (; t + TU <= tend; t += TU) {
-    float xv[TU][CPT];
-#pragma unroll
-    for (int u = 0; u < TU; ++u) load_x(t + u, xv[u]);
-#pragma unroll
-    for (int u = 0; u < TU; ++u) token(t + u, xv[u]);
-  }
-  for (; t < tend; ++t) {
-    float xr[CPT];
-    load_x(t, xr);
-    token(t, xr);
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-#pragma unroll
-      for (int e = 0; e < EP; ++e) red[wave - 1][c * EP + e][lane] = acc[c][e];
-  }
-  __syncthreads();
-  if (wave == 0 && col_ok) {
-#pragma unroll
-    for (int w = 0; w < kRwgWaves - 1; ++w)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c)
-#pragma unroll
-        for (int e = 0; e < EP; ++e) acc[c][e] += red[w][c * EP + e][lane];
-    float* p = partial + ((int64_t)blockIdx.y * d + i0) * E;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-#pragma unroll
-      for (int e = 0; e < EP; ++e)
-        if (FULL || e < E) p[c * E + e] = acc[c][e];
-  }
-}
 
 // partial[b][i][e] on the fp32 matrix cores: v_mfma_f32_16x16x4_f32 takes
 // A[m][kk] from lane kk * 16 + m and B[kk][n] from lane kk * 16 + n, so 4
@@ -297,26 +207,6 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 }
 
 template <typename T, int EP>
-static hipError_t launch_rwg(const RouteBwdArgs& a, hipStream_t st) {
-  constexpr int CPT = 64 / EP;
-  const int nb = router_wgrad_blocks(a.T);
-  const int tw = (int)((a.T + (int64_t)nb * kRwgWaves - 1) / ((int64_t)nb * kRwgWaves));  // tokens per wave
-  const dim3 grid((unsigned)((a.d + 64 * CPT - 1) / (64 * CPT)), nb);
-  if (a.E == EP)
-    hipLaunchKernelGGL((router_wgrad_partial_kernel<T, EP, CPT, true>), grid, dim3(64 * kRwgWaves), 0, st,
-                       (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d, a.E, tw);
-  else
-    hipLaunchKernelGGL((router_wgrad_partial_kernel<T, EP, CPT, false>), grid, dim3(64 * kRwgWaves), 0, st,
-                       (const T*)a.x, a.dlogits, a.partial, a.T, (int)a.d, a.E, tw);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t dE = a.d * a.E;
-  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
-                     a.partial, nb, dE, (T*)a.dw_router);
-  return hipGetLastError();
-}
-
-template <typename T, int EP>
 static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
   constexpr int V = Vec16<T>::N, CW = 16 * V;
   constexpr size_t lds = (size_t)2 * V * (EP / 16) * 4 * 64 * 4;
@@ -339,7 +229,7 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// partial[b][i][e] on the bf16 matrix cores (bf16 x, more than 16 experts):
+// partial[b][i][e] on the bf16 matrix cores (bf16 x; E padded to 16, 32 or 64):
 // v_mfma_f32_16x16x32_bf16 with M = 16 columns of x, N = 16 experts and K =
 // 32 tokens.  dlogits enter as bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi),
 // one MFMA each), which keeps about 16 significant bits; products of bf16
@@ -365,11 +255,14 @@ __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* 
   constexpr int XP = kRwbCols * 2 + 32;  // x tile row pitch in bytes: the +32 puts the 4 K rows of a read on other banks
   constexpr int DP = EP * 2 + 32;        // hi / lo tile row pitch
   constexpr int XB = 32 * XP, DB = 32 * DP, BUF = XB + 2 * DB;
-  constexpr int DQ = EP / 4, DR = 256 / DQ, DPASS = 32 / DR;  // dlogits: 4 experts per thread, DR rows per pass
+  // dlogits: 4 experts per thread, DR rows per pass (with 16 experts only the
+  // first 128 threads carry them)
+  constexpr int DQ = EP / 4, DR = 256 / DQ < 32 ? 256 / DQ : 32, DPASS = 32 / DR;
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = blockIdx.x * kRwbCols;
+  const bool dthr = tid / DQ < DR;
   const int64_t tbeg = (int64_t)blockIdx.y * tb;
   const int64_t tend = tbeg + tb < Tn ? tbeg + tb : Tn;
   const int nsteps = tend > tbeg ? (int)((tend - tbeg + 31) / 32) : 0;
@@ -415,8 +308,10 @@ __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* 
         l[q] = bf16_bits(dv[p][q] - __uint_as_float(h[q] << 16));
       }
       const int off = (tid / DQ + DR * p) * DP + de * 2;
-      *reinterpret_cast<u32x2*>(buf + XB + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(buf + XB + DB + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      if (dthr) {
+        *reinterpret_cast<u32x2*>(buf + XB + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *reinterpret_cast<u32x2*>(buf + XB + DB + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      }
     }
   };
 
@@ -488,15 +383,17 @@ static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// bf16 x with up to 16 experts: the vector kernel, bound by reading x (the
-// fp32 MFMA pads E to 16 and measured slower on the Mixtral shape, 0.059
-// against 0.049 ms for the whole router backward).  bf16 x with more experts:
-// the bf16 MFMA kernel with dlogits as hi + lo (DeepSeek-V2-Lite shape: 0.14
-// ms on the fp32 MFMA kernel, 0.05 ms).  fp32 x: the fp32 MFMA kernel.
+// bf16 x: the bf16 MFMA kernel with dlogits as hi + lo, E padded to 16, 32
+// or 64.  Up to 16 experts it replaced the vector kernel (route backward,
+// warm / cold caches: GPT-2 24.8 / 30.1 -> 16.9 / 24.9 us, BERT-L 36.3 / 40.7
+// -> 22.5 / 28.3 us, Mixtral 39.2 / 45.0 -> 36.0 / 45.4 us); with more
+// experts it replaced the fp32 MFMA kernel (DeepSeek-V2-Lite 0.14 -> 0.05 ms).
+// fp32 x: the fp32 MFMA kernel.
 template <typename T>
 static hipError_t launch_rwg_dt(const RouteBwdArgs& a, hipStream_t st) {
-  if (sizeof(T) == 2 && a.E <= 8) return launch_rwg<T, 8>(a, st);
-  if (sizeof(T) == 2 && a.E <= 16) return launch_rwg<T, 16>(a, st);
+  if constexpr (sizeof(T) == 2) {
+    if (a.E <= 16) return launch_rwg_bf16mfma<16>(a, st);
+  }
   if (a.E <= 16) return launch_rwg_mfma<T, 16>(a, st);
   if constexpr (sizeof(T) == 2) {
     if (a.E <= 32) return launch_rwg_bf16mfma<32>(a, st);
