@@ -261,6 +261,122 @@ __global__ __launch_bounds__(256) void pack_router_frags_kernel(const uint16_t* 
   wf[i] = u32x4{v[0], v[1], v[2], v[3]};
 }
 
+// The value of the partner lane of step S of an all-reduce over groups of L
+// lanes (L = 4, 8 or 16), by DPP within each row of 16 lanes: step 0 takes
+// lane l ^ 1, step 1 lane l ^ 2 (quad permutations [1, 0, 3, 2] and
+// [2, 3, 0, 1]), step 2 the mirror within 8 lanes (quad 0 with quad 1) and
+// step 3 the mirror within 16 (the two groups of 8).  After steps 0 .. log2 L
+// - 1, combining with a commutative operation, every lane of a group holds
+// the same result.
+template <int S>
+__device__ __forceinline__ int group_step(int v) {
+  constexpr int ctrl = S == 0 ? 0xB1 : S == 1 ? 0x4E : S == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+template <int S>
+__device__ __forceinline__ float group_step(float v) {
+  return __int_as_float(group_step<S>(__float_as_int(v)));
+}
+template <int L> constexpr int group_steps() { return L == 4 ? 2 : L == 8 ? 3 : 4; }
+
+// (value, expert) of the better of two candidates: the larger value, then
+// the lower expert index
+__device__ __forceinline__ void better_of(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+
+// End of routing for a token spread over a group of L lanes (L = 4, 8 or 16),
+// four experts per lane: lane part p = lane % L holds the summed products of
+// token t for experts e0 .. e0 + 3, e0 = 4 p, and the same bias entries in
+// bq.  The same results as finish_token: bias, logits row, softmax
+// statistics, k rounds of arg-max by (value desc, index asc), gate weights;
+// the statistics and each round's pick are combined over the group's lanes
+// with DPP (group_step).  Round j's pick is stored by part j % L.
+template <int L>
+__device__ __forceinline__ void finish_group(const f32x4& acc, const float (&bq)[4], int64_t t, int64_t Tn, int e0,
+                                             int E, int k, int gating, float* __restrict__ logits,
+                                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int NS = group_steps<L>(), SLOTS = (8 + L - 1) / L;
+  float v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = e0 + c < E ? acc[c] + bq[c] : -INFINITY;
+  const bool live = t < Tn;
+  if (live) {
+    float* lrow = logits + t * E + e0;
+    if ((E & 3) == 0) {
+      if (e0 < E) st16(lrow, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                   __float_as_uint(v[3])});
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e0 + c < E) lrow[c] = v[c];
+    }
+  }
+  // softmax statistics over the token's experts
+  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  mx = fmaxf(mx, group_step<0>(mx));
+  mx = fmaxf(mx, group_step<1>(mx));
+  if constexpr (NS > 2) mx = fmaxf(mx, group_step<2>(mx));
+  if constexpr (NS > 3) mx = fmaxf(mx, group_step<3>(mx));
+  float z = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (e0 + c < E) z += __expf(v[c] - mx);
+  z += group_step<0>(z);
+  z += group_step<1>(z);
+  if constexpr (NS > 2) z += group_step<2>(z);
+  if constexpr (NS > 3) z += group_step<3>(z);
+
+  // k rounds of arg-max; every lane of the token sees each round's pick
+  const int part = e0 >> 2;
+  unsigned taken = 0;
+  int my_e[SLOTS];
+  float my_v[SLOTS];
+#pragma unroll
+  for (int r = 0; r < SLOTS; ++r) {
+    my_e[r] = 0;
+    my_v[r] = 0.0f;
+  }
+  float v0 = 0.0f, den = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      float bv = -INFINITY;
+      int be = 1 << 30;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e0 + c < E && !((taken >> c) & 1u) && (be == (1 << 30) || v[c] > bv)) {
+          bv = v[c];
+          be = e0 + c;
+        }
+      better_of(bv, be, group_step<0>(bv), group_step<0>(be));
+      better_of(bv, be, group_step<1>(bv), group_step<1>(be));
+      if constexpr (NS > 2) better_of(bv, be, group_step<2>(bv), group_step<2>(be));
+      if constexpr (NS > 3) better_of(bv, be, group_step<3>(bv), group_step<3>(be));
+      if (be >= e0 && be < e0 + 4) taken |= 1u << (be - e0);
+      if (j == 0) v0 = bv;
+      den += __expf(bv - v0);
+      if (j % L == part) {
+        my_e[j / L] = be;
+        my_v[j / L] = bv;
+      }
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int r = 0; r < SLOTS; ++r) {
+    const int j = L * r + part;
+    if (j < k) {
+      const float gw = gating == 0 ? __expf(my_v[r] - mx) / z : __expf(my_v[r] - v0) / den;
+      topk_idx[t * k + j] = my_e[r];
+      topk_w[t * k + j] = gw;
+    }
+  }
+}
+
 // A workgroup owns 16 TG tokens; its 8 waves take every 8th 32-K block, each
 // keeping the x and W blocks of the next P K blocks in flight.  The waves' accumulators are summed in a
 // fixed binary tree through LDS (deterministic logits), wave 0 spreads them
@@ -356,25 +472,30 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_mfma_kernel(
     }
     __syncthreads();
   }
-  if (wave != 0) return;
-  // accumulator (tg, nb)[q] of lane l: token 16 tg + 4 (l / 16) + q, expert 16 nb + l % 16
-  float* tab = red;  // [TOK][EP], reused: only wave 0 is left
+  // accumulator (tg, nb)[q] of wave 0's lane l: token 16 tg + 4 (l / 16) + q,
+  // expert 16 nb + l % 16, spread into a [16 TG][EP] table
+  float* tab = red;  // reused: the tree's reads are done
+  if (wave == 0) {
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg)
+    for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tab[(16 * tg + 4 * g + q) * EP + 16 * nb + (lane & 15)] = acc[tg][nb][q];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int64_t t = t0 + lane;
-  if (lane >= TOK || t >= Tn) return;
-  float lv[EP];
+        for (int q = 0; q < 4; ++q) tab[(16 * tg + 4 * g + q) * EP + 16 * nb + (lane & 15)] = acc[tg][nb][q];
+  }
+  __syncthreads();
+  // every wave finishes tokens, L = EP / 4 lanes per token (four experts a
+  // lane), 64 / L tokens per pass
+  constexpr int L = EP / 4, TPP = 64 / L, PASSES = TOK / TPP;
+  const int e0 = 4 * (lane % L);
+  float bq[4];
 #pragma unroll
-  for (int e = 0; e < EP; ++e) lv[e] = tab[lane * EP + e];
-  if (E == EP) finish_token<EP, true>(lv, t, E, k, gating, bias, logits, topk_idx, topk_w);
-  else finish_token<EP, false>(lv, t, E, k, gating, bias, logits, topk_idx, topk_w);
+  for (int c = 0; c < 4; ++c) bq[c] = (bias && e0 + c < E) ? bias[e0 + c] : 0.0f;
+  for (int p = wave; p < PASSES; p += kMfmaWaves) {
+    const int tt = p * TPP + lane / L;
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(tab + tt * EP + e0);
+    finish_group<L>(v4, bq, t0 + tt, Tn, e0, E, k, gating, logits, topk_idx, topk_w);
+  }
 }
 
 static hipError_t pack_router_frags(const RouteArgs& a, int NB, hipStream_t st) {
@@ -412,101 +533,6 @@ static hipError_t pack_router_frags(const RouteArgs& a, int NB, hipStream_t st) 
 // (the other two quadrants are unused).  One MFMA still covers 1 KB of x,
 // and the fragments of a 64-K line fill all 16 columns (half the registers).
 // ---------------------------------------------------------------------------
-// value of lane l ^ 1 (XM = 1) or l ^ 2 (XM = 2) within each group of four
-template <int XM>
-__device__ __forceinline__ int quad_xor(int v) {
-  // DPP quad permutations [1, 0, 3, 2] and [2, 3, 0, 1]
-  return __builtin_amdgcn_update_dpp(0, v, XM == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false);
-}
-template <int XM>
-__device__ __forceinline__ float quad_xor(float v) {
-  return __int_as_float(quad_xor<XM>(__float_as_int(v)));
-}
-
-// (value, expert) of the better of two candidates: the larger value, then
-// the lower expert index
-__device__ __forceinline__ void better_of(float& v, int& e, float ov, int oe) {
-  if (ov > v || (ov == v && oe < e)) {
-    v = ov;
-    e = oe;
-  }
-}
-
-// End of routing for 16 tokens spread over a wave, four lanes per token: lane
-// l holds the summed products of token t for experts e0 .. e0 + 3, e0 =
-// 4 (l % 4), and the same bias entries in bq.  The same results as
-// finish_token: bias, logits row, softmax statistics, k rounds of arg-max by
-// (value desc, index asc), gate weights; the statistics are combined across
-// the four lanes with xor shuffles.  Round j's pick is stored by lane j % 4.
-__device__ __forceinline__ void finish_quad(const f32x4& acc, const float (&bq)[4], int64_t t, int64_t Tn, int e0,
-                                            int E, int k, int gating, float* __restrict__ logits,
-                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  float v[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) v[c] = e0 + c < E ? acc[c] + bq[c] : -INFINITY;
-  const bool live = t < Tn;
-  if (live) {
-    float* lrow = logits + t * E + e0;
-    if ((E & 3) == 0) {
-      if (e0 < E) st16(lrow, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                   __float_as_uint(v[3])});
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (e0 + c < E) lrow[c] = v[c];
-    }
-  }
-  // softmax statistics over the token's experts
-  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-  mx = fmaxf(mx, quad_xor<1>(mx));
-  mx = fmaxf(mx, quad_xor<2>(mx));
-  float z = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (e0 + c < E) z += __expf(v[c] - mx);
-  z += quad_xor<1>(z);
-  z += quad_xor<2>(z);
-
-  // k rounds of arg-max; every lane of the token sees each round's pick
-  const int part = e0 >> 2;
-  unsigned taken = 0;
-  int my_e[2] = {0, 0};
-  float my_v[2] = {0.0f, 0.0f};
-  float v0 = 0.0f, den = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      float bv = -INFINITY;
-      int be = 1 << 30;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (e0 + c < E && !((taken >> c) & 1u) && (be == (1 << 30) || v[c] > bv)) {
-          bv = v[c];
-          be = e0 + c;
-        }
-      better_of(bv, be, quad_xor<1>(bv), quad_xor<1>(be));
-      better_of(bv, be, quad_xor<2>(bv), quad_xor<2>(be));
-      if (be >= e0 && be < e0 + 4) taken |= 1u << (be - e0);
-      if (j == 0) v0 = bv;
-      den += __expf(bv - v0);
-      if ((j & 3) == part) {
-        my_e[j >> 2] = be;
-        my_v[j >> 2] = bv;
-      }
-    }
-  }
-  if (!live) return;
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int j = 4 * r + part;
-    if (j < k) {
-      const float gw = gating == 0 ? __expf(my_v[r] - mx) / z : __expf(my_v[r] - v0) / den;
-      topk_idx[t * k + j] = my_e[r];
-      topk_w[t * k + j] = gw;
-    }
-  }
-}
-
 __device__ __forceinline__ void lds_only_barrier() {
   // orders LDS traffic only: outstanding global loads stay in flight
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -733,7 +759,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void route_stream_kernel(
       } else {
         v4 = *reinterpret_cast<const f32x4*>(tab + tt * 16 + e0);
       }
-      finish_quad(v4, bq, (s0 + i * ds) * TOKS + 16 * slot + tt, Tn, e0, E, k, gating, logits, topk_idx, topk_w);
+      finish_group<4>(v4, bq, (s0 + i * ds) * TOKS + 16 * slot + tt, Tn, e0, E, k, gating, logits, topk_idx,
+                      topk_w);
     }
     // the loads of step i + 2 go out after the finish, which uses their
     // registers meanwhile (issuing them before the barrier measured slower)
