@@ -78,6 +78,8 @@ hipError_t launch_route_bwd(const RouteBwdArgs& a, bool bf16_dtype, hipStream_t 
 hipError_t launch_dispatch_bwd(const DispatchBwdArgs& a, bool bf16_dtype, hipStream_t st);
 
 int router_wgrad_blocks(int64_t T);
+// compute units of the current device (asked once per device)
+hipError_t device_cus(int* cus);
 
 hipError_t launch_aux_loss(const AuxArgs& a, hipStream_t st);
 hipError_t launch_aux_loss_bwd(const AuxArgs& a, hipStream_t st);

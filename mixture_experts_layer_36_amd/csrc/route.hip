@@ -533,22 +533,14 @@ static hipError_t pack_router_frags(const RouteArgs& a, int NB, hipStream_t st) 
 // (the other two quadrants are unused).  One MFMA still covers 1 KB of x,
 // and the fragments of a 64-K line fill all 16 columns (half the registers).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lds_only_barrier() {
-  // orders LDS traffic only: outstanding global loads stay in flight
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <bool PAIRS> constexpr int stream_nh() { return PAIRS ? 2 : 1; }  // accumulators per lane
 template <bool PAIRS> constexpr int stream_red_bytes() { return 2 * kMfmaWaves * stream_nh<PAIRS>() * 64 * 16; }
 template <bool PAIRS> constexpr int stream_tab_bytes() { return kMfmaWaves * stream_nh<PAIRS>() * 256 * 4; }
 constexpr int kStreamMaxLds = 4096 * 32;  // W_r rows of up to 16 experts for d = 4096
 
-constexpr int kLdsPerCu = 160 * 1024;
 
 // compute units of the current device (asked once per device)
-static hipError_t device_cus(int* cus) {
+hipError_t device_cus(int* cus) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> count[kMaxDev] = {};
   int dev = 0;

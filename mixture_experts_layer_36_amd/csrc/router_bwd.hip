@@ -9,8 +9,8 @@
 //                          dl[e_j] = g_j * (dg_j - sum_m g_m dg_m), 0 elsewhere
 // router wgrad: dW_r = x^T dl as a deterministic two-stage reduction over
 //   tokens: each block of tokens writes an fp32 partial [d, E] (bf16 MFMA for
-//   bf16 x, fp32 MFMA for fp32 x), then the partials are summed in block
-//   order (at most 64 blocks).
+//   bf16 x, fp32 MFMA for fp32 x), then the partials (at most 64 blocks) are
+//   summed in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -176,34 +176,48 @@ __global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_mfma_kernel(const
       }
 }
 
-// dw[i] = sum over b in order of partial[b][i].  A thread owns 4 consecutive
-// outputs and loads all its partials (nb <= 64, 16-byte loads) before the
-// in-order sums, so the loads overlap instead of following one another.
+// dw[i] = the sum of partial[b][i] over the nb <= 64 token blocks, in a fixed
+// order.  A workgroup owns 64 consecutive outputs (16 quads); its 256 threads
+// are 16 slices x 16 quads: slice s adds blocks 4 s .. 4 s + 3 in order (its
+// 16-byte loads issued together), the four slices of a wave meet in an xor
+// tree (s with s ^ 1, then pairs with pairs) and the four waves' sums are
+// added as (w0 + w1) + (w2 + w3).  Floating-point addition commutes exactly,
+// so every run gives the same bits.  dE is a multiple of 8: a quad is all in
+// or all out.
 template <typename T>
 __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ partial, int nb,
                                                                   int64_t dE, T* __restrict__ dw) {
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i0 >= dE) return;
-  if (i0 + 4 <= dE && (dE & 3) == 0) {
-    f32x4 v[64];
+  __shared__ f32x4 red[4][16];
+  const int tid = threadIdx.x, q = tid & 15, sl = tid >> 4, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = ((int64_t)blockIdx.x * 16 + q) * 4;
+  const bool ok = i0 < dE;
+  f32x4 v[4];
 #pragma unroll
-    for (int b = 0; b < 64; ++b)
-      if (b < nb) v[b] = *reinterpret_cast<const f32x4*>(partial + (int64_t)b * dE + i0);
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int b = 0; b < 64; ++b)
-      if (b < nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s[q] += v[b][q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dw[i0 + q] = from_f32<T>(s[q]);
-  } else {
-    for (int64_t i = i0; i < i0 + 4 && i < dE; ++i) {
-      float s = 0.0f;
-      for (int b = 0; b < nb; ++b) s += partial[(int64_t)b * dE + i];
-      dw[i] = from_f32<T>(s);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int b = 4 * sl + r;
+    const f32x4 w = *reinterpret_cast<const f32x4*>(partial + (int64_t)(b < nb ? b : 0) * dE + (ok ? i0 : 0));
+    v[r] = (ok && b < nb) ? w : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  f32x4 sum = ((v[0] + v[1]) + v[2]) + v[3];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sum[c] += __shfl_xor(sum[c], 16);
+    sum[c] += __shfl_xor(sum[c], 32);
+  }
+  if (lane < 16) red[wave][q] = sum;
+  __syncthreads();
+  if (tid >= 16 || !ok) return;
+  const f32x4 r = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) dw[i0 + c] = from_f32<T>(r[c]);
+}
+
+template <typename T>
+static hipError_t launch_rwg_reduce(const RouteBwdArgs& a, int nb, hipStream_t st) {
+  const int64_t dE = a.d * a.E;
+  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 63) / 64)), dim3(256), 0, st,
+                     a.partial, nb, dE, (T*)a.dw_router);
+  return hipGetLastError();
 }
 
 template <typename T, int EP>
@@ -223,10 +237,7 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
                      a.E, tw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t dE = a.d * a.E;
-  hipLaunchKernelGGL((router_wgrad_reduce_kernel<T>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
-                     a.partial, nb, dE, (T*)a.dw_router);
-  return hipGetLastError();
+  return launch_rwg_reduce<T>(a, nb, st);
 }
 
 // partial[b][i][e] on the bf16 matrix cores (bf16 x; E padded to 16, 32 or 64):
@@ -234,78 +245,88 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
 // 32 tokens.  dlogits enter as bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi),
 // one MFMA each), which keeps about 16 significant bits; products of bf16
 // values are exact in the fp32 accumulators.  Both operands are token-major
-// in memory, so each 32-token step stages x[32][256 columns] and hi / lo
-// [32][EP] in LDS (two buffers, one barrier per step: a buffer is rewritten
-// only after every wave has passed the barrier that follows its last reads),
-// and the fragments come out transposed by ds_read_b64_tr_b16: within a
-// 16-lane group, lane j addresses 4 consecutive columns of K row j / 4 of a
-// 4 x 16 block and lane i receives column i's 4 K values, so two reads give a
-// lane the 8 consecutive tokens of its MFMA operand.  A workgroup of 4 waves
-// owns 256 columns (64 per wave) for all experts and tb tokens; the next
-// step's global loads are in flight while the current one is multiplied.
-constexpr int kRwbCols = 256;
+// in memory, so each 32-token step stages x[32][64 NW columns] and hi / lo
+// [32][EP] in LDS, and the fragments come out transposed by
+// ds_read_b64_tr_b16: within a 16-lane group, lane j addresses 4 consecutive
+// columns of K row j / 4 of a 4 x 16 block and lane i receives column i's 4 K
+// values, so two reads give a lane the 8 consecutive tokens of its MFMA
+// operand.  A workgroup of NW waves owns 64 NW columns (64 per wave) for all
+// experts and tb tokens, so every token contributes a row run of 128 NW
+// bytes.  Two register sets hold the global loads of the next two steps:
+// step s + 2 is issued right after step s is in LDS, and the barriers order
+// LDS traffic only, so those loads stay in flight across them.  Two LDS
+// buffers, one barrier per step: a buffer is rewritten only after every wave
+// has passed the barrier that follows its last reads.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-template <int EP>
-__global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* __restrict__ x,
-                                                                   const float* __restrict__ dl,
-                                                                   float* __restrict__ partial, int64_t Tn, int d,
-                                                                   int E, int tb) {
-  constexpr int NB = EP / 16;
-  constexpr int XP = kRwbCols * 2 + 32;  // x tile row pitch in bytes: the +32 puts the 4 K rows of a read on other banks
-  constexpr int DP = EP * 2 + 32;        // hi / lo tile row pitch
-  constexpr int XB = 32 * XP, DB = 32 * DP, BUF = XB + 2 * DB;
-  // dlogits: 4 experts per thread, DR rows per pass (with 16 experts only the
-  // first 128 threads carry them)
-  constexpr int DQ = EP / 4, DR = 256 / DQ < 32 ? 256 / DQ : 32, DPASS = 32 / DR;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+template <int EP, int NW>
+struct RwbShape {
+  static constexpr int NT = 64 * NW, COLS = 64 * NW;
+  static constexpr int CPR = COLS / 8;            // 16-byte chunks per x row
+  static constexpr int XP = COLS * 2 + 32;        // x row pitch in bytes: the +32 puts the 4 K rows of a read on other banks
+  static constexpr int DP = EP * 2 + 32;          // hi / lo row pitch
+  static constexpr int XB = 32 * XP, DB = 32 * DP, BUF = XB + 2 * DB;
+  static constexpr int LDS = 2 * BUF;
+  // dlogits: 4 experts per thread, DR rows per pass
+  static constexpr int DQ = EP / 4, DR = NT / DQ < 32 ? NT / DQ : 32, DPASS = 32 / DR;
+};
+
+template <int EP, int NW>
+__global__ __launch_bounds__(64 * NW) void router_wgrad_bf16mfma_kernel(const bf16* __restrict__ x,
+                                                                       const float* __restrict__ dl,
+                                                                       float* __restrict__ partial, int64_t Tn, int d,
+                                                                       int E, int tb) {
+  using S = RwbShape<EP, NW>;
+  constexpr int NB = EP / 16, CPR = S::CPR, XP = S::XP, DP = S::DP, XB = S::XB, DB = S::DB, BUF = S::BUF;
+  constexpr int DQ = S::DQ, DR = S::DR, DPASS = S::DPASS;
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = blockIdx.x * kRwbCols;
+  const int c0 = blockIdx.x * S::COLS;
   const bool dthr = tid / DQ < DR;
   const int64_t tbeg = (int64_t)blockIdx.y * tb;
   const int64_t tend = tbeg + tb < Tn ? tbeg + tb : Tn;
   const int nsteps = tend > tbeg ? (int)((tend - tbeg + 31) / 32) : 0;
 
-  // global -> registers for one step: x rows tid / 32 + 8 p, 16-byte chunk
-  // tid % 32; dlogits rows tid / DQ + DR p, experts 4 (tid % DQ) .. + 3
-  // (unconditional loads from valid addresses, zeros by select)
-  const int xcol = c0 + (tid & 31) * 8;
+  // global -> registers for one step: x rows tid / CPR + 8 p, 16-byte chunk
+  // tid % CPR; dlogits rows tid / DQ + DR p, experts 4 (tid % DQ) .. + 3.
+  // The loads are unconditional, from valid addresses; the zeros past the
+  // token range, the last column or E are selected when the registers are
+  // written to LDS, so that no select waits for a load in flight.
+  const int xcol = c0 + (tid % CPR) * 8;
   const bool xcol_ok = xcol < d;  // d is a multiple of 8: a chunk is all in or all out
   const int de = 4 * (tid % DQ);
-  u32x4 xr[4];
-  float dv[DPASS][4];
-  auto gload = [&](int s) {
+  auto gload = [&](int s, u32x4 (&xr)[4], float (&dv)[DPASS][4]) {
     const int64_t t0 = tbeg + 32 * s;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int64_t t = t0 + (tid >> 5) + 8 * p;
-      const bool ok = xcol_ok && t < tend;
-      const u32x4 v = ld16(x + (t < tend ? t : tbeg) * d + (xcol_ok ? xcol : 0));
-      xr[p] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      const int64_t t = t0 + tid / CPR + 8 * p;
+      xr[p] = ld16(x + (t < tend ? t : tbeg) * d + (xcol_ok ? xcol : 0));
     }
 #pragma unroll
     for (int p = 0; p < DPASS; ++p) {
       const int64_t t = t0 + tid / DQ + DR * p;
       const int64_t tc = t < tend ? t : tbeg;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = t < tend && de + q < E;
-        const float v = dl[tc * E + (de + q < E ? de + q : 0)];
-        dv[p][q] = ok ? v : 0.0f;
-      }
+      for (int q = 0; q < 4; ++q) dv[p][q] = dl[tc * E + (de + q < E ? de + q : 0)];
     }
   };
-  auto lwrite = [&](char* buf) {
+  auto lwrite = [&](char* buf, int s, const u32x4 (&xr)[4], const float (&dv)[DPASS][4]) {
+    const int64_t t0 = tbeg + 32 * s;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) st16(buf + ((tid >> 5) + 8 * p) * XP + (tid & 31) * 16, xr[p]);
+    for (int p = 0; p < 4; ++p) {
+      const bool ok = xcol_ok && t0 + tid / CPR + 8 * p < tend;
+      st16(buf + (tid / CPR + 8 * p) * XP + (tid % CPR) * 16, ok ? xr[p] : u32x4{0u, 0u, 0u, 0u});
+    }
 #pragma unroll
     for (int p = 0; p < DPASS; ++p) {
+      const bool tok = t0 + tid / DQ + DR * p < tend;
       uint32_t h[4], l[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        h[q] = bf16_bits(dv[p][q]);
-        l[q] = bf16_bits(dv[p][q] - __uint_as_float(h[q] << 16));
+        const float v = tok && de + q < E ? dv[p][q] : 0.0f;
+        h[q] = bf16_bits(v);
+        l[q] = bf16_bits(v - __uint_as_float(h[q] << 16));
       }
       const int off = (tid / DQ + DR * p) * DP + de * 2;
       if (dthr) {
@@ -324,12 +345,7 @@ __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* 
   // column 4 (j % 4) of the 16-column block (G = lane / 16, j = lane % 16)
   const int G = lane >> 4, j = lane & 15;
   const int kr = 8 * G + (j >> 2), cq = 4 * (j & 3);
-  if (nsteps > 0) gload(0);
-  for (int s = 0; s < nsteps; ++s) {
-    char* buf = lds + (s & 1) * BUF;
-    lwrite(buf);
-    __syncthreads();
-    if (s + 1 < nsteps) gload(s + 1);
+  auto compute = [&](const char* buf) {
     u32x4 a[4], bh[NB], bl[NB];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -354,6 +370,42 @@ __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* 
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[mb]),
                                                               __builtin_bit_cast(bf16x8_t, bl[nb]), acc[mb][nb], 0, 0, 0);
       }
+  };
+  // Register set A carries even steps, B odd ones.  Every load of the first
+  // two steps and of the main loop is unconditional (a step past the range
+  // reads valid rows that lwrite zeroes), so that the compiler's wait counts
+  // see the same loads in flight on every path into the loop: A's loads are
+  // then awaited with B's still outstanding.
+  if (nsteps == 0) return;
+  u32x4 xa[4], xb[4];
+  float da[DPASS][4], db[DPASS][4];
+  gload(0, xa, da);
+  gload(1, xb, db);
+  int s = 0;
+  for (; s + 3 < nsteps; s += 2) {
+    lwrite(lds, s, xa, da);
+    lds_only_barrier();
+    gload(s + 2, xa, da);
+    compute(lds);
+    lwrite(lds + BUF, s + 1, xb, db);
+    lds_only_barrier();
+    gload(s + 3, xb, db);
+    compute(lds + BUF);
+  }
+  // the last one to three steps
+  lwrite(lds, s, xa, da);
+  lds_only_barrier();
+  if (s + 2 < nsteps) gload(s + 2, xa, da);
+  compute(lds);
+  if (s + 1 < nsteps) {
+    lwrite(lds + BUF, s + 1, xb, db);
+    lds_only_barrier();
+    compute(lds + BUF);
+  }
+  if (s + 2 < nsteps) {
+    lwrite(lds, s + 2, xa, da);
+    lds_only_barrier();
+    compute(lds);
   }
   // accumulator (mb, nb)[q] of lane l: column 64 wave + 16 mb + 4 (l / 16) + q, expert 16 nb + l % 16
   float* pb = partial + (int64_t)blockIdx.y * d * E;
@@ -368,19 +420,43 @@ __global__ __launch_bounds__(256) void router_wgrad_bf16mfma_kernel(const bf16* 
       }
 }
 
-template <int EP>
-static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
-  const int nb = router_wgrad_blocks(a.T);
-  const int tb = (int)((a.T + nb - 1) / nb);  // tokens per block
-  const dim3 grid((unsigned)((a.d + kRwbCols - 1) / kRwbCols), nb);
-  hipLaunchKernelGGL((router_wgrad_bf16mfma_kernel<EP>), grid, dim3(256), 0, st, (const bf16*)a.x, a.dlogits,
+// Workgroups of the bf16 kernel that fit on one compute unit (LDS bound).
+template <int EP, int NW>
+constexpr int rwb_per_cu() {
+  return kLdsPerCu / RwbShape<EP, NW>::LDS;
+}
+
+template <int EP, int NW>
+static hipError_t launch_rwg_bf16mfma_nw(const RouteBwdArgs& a, int nb, hipStream_t st) {
+  using S = RwbShape<EP, NW>;
+  const int64_t tb0 = (a.T + nb - 1) / nb;
+  const int tb = (int)((tb0 + 31) / 32 * 32);   // tokens per block, whole steps
+  const int nbr = (int)((a.T + tb - 1) / tb);  // blocks that hold tokens
+  const dim3 grid((unsigned)((a.d + S::COLS - 1) / S::COLS), nbr);
+  hipLaunchKernelGGL((router_wgrad_bf16mfma_kernel<EP, NW>), grid, dim3(S::NT), 0, st, (const bf16*)a.x, a.dlogits,
                      a.partial, a.T, (int)a.d, a.E, tb);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t dE = a.d * a.E;
-  hipLaunchKernelGGL((router_wgrad_reduce_kernel<bf16>), dim3((unsigned)((dE + 1023) / 1024)), dim3(256), 0, st,
-                     a.partial, nb, dE, (bf16*)a.dw_router);
-  return hipGetLastError();
+  return launch_rwg_reduce<bf16>(a, nbr, st);
+}
+
+// Column width: the widest block (longest row runs) whose workgroups still
+// give every compute unit one; token blocks: as many as fill the resident
+// slots once, at most router_wgrad_blocks(T) (the planned partials).
+template <int EP>
+static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
+  int cus = 0;
+  hipError_t err = device_cus(&cus);
+  if (err != hipSuccess) return err;
+  const int nbmax = router_wgrad_blocks(a.T);
+  auto blocks = [&](int cols, int per_cu) {
+    const int64_t cb = (a.d + cols - 1) / cols;
+    int64_t nb = ((int64_t)cus * per_cu + cb - 1) / cb;
+    return (int)(nb < 1 ? 1 : nb > nbmax ? nbmax : nb);
+  };
+  if ((a.d + 511) / 512 * nbmax >= cus) return launch_rwg_bf16mfma_nw<EP, 8>(a, blocks(512, rwb_per_cu<EP, 8>()), st);
+  if ((a.d + 255) / 256 * nbmax >= cus) return launch_rwg_bf16mfma_nw<EP, 4>(a, blocks(256, rwb_per_cu<EP, 4>()), st);
+  return launch_rwg_bf16mfma_nw<EP, 2>(a, blocks(128, rwb_per_cu<EP, 2>()), st);
 }
 
 // bf16 x: the bf16 MFMA kernel with dlogits as hi + lo, E padded to 16, 32
@@ -388,6 +464,10 @@ static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
 // warm / cold caches: GPT-2 24.8 / 30.1 -> 16.9 / 24.9 us, BERT-L 36.3 / 40.7
 // -> 22.5 / 28.3 us, Mixtral 39.2 / 45.0 -> 36.0 / 45.4 us); with more
 // experts it replaced the fp32 MFMA kernel (DeepSeek-V2-Lite 0.14 -> 0.05 ms).
+// Column blocks of up to 512, two steps of loads in flight, a grid sized to
+// the resident slots and the 16-way reduce then took the route backward
+// inside full steps from 26.5 to 15.9 us (GPT-2), 31.3 to 22.2 (BERT-L), 50.9
+// to 45.5 (Mixtral) and 50.2 to 41.0 (DeepSeek-V2-Lite).
 // fp32 x: the fp32 MFMA kernel.
 template <typename T>
 static hipError_t launch_rwg_dt(const RouteBwdArgs& a, hipStream_t st) {
@@ -404,7 +484,7 @@ static hipError_t launch_rwg_dt(const RouteBwdArgs& a, hipStream_t st) {
 }
 
 int router_wgrad_blocks(int64_t T) {
-  int64_t nb = (T + 255) / 256;
+  int64_t nb = (T + 127) / 128;
   if (nb > 64) nb = 64;
   if (nb < 1) nb = 1;
   return (int)nb;
