@@ -34,10 +34,29 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict
   const bool tok = t < Tn;  // every lane stays for the group reductions
   const bool valid = tok && e < E;
   const float l = valid ? logits[t * E + e] : -INFINITY;
+  const float add = dl_add && valid ? dl_add[t * E + e] : 0.0f;
+  // the token's k choices and their gradients, four at a time, all loads of
+  // a group issued together (a gradient is not fetched after its index is
+  // known; clamped indices keep every load in the token's row)
+  const int64_t tc = tok ? t : 0;
   int sel = -1;
-  for (int j = 0; j < k; ++j)
-    if (tok && idx[t * k + j] == e) sel = j;
-  const float dgl = sel >= 0 ? dg[t * k + sel] : 0.0f;
+  float dgl = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int ij[4];
+    float gj[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u < k ? j0 + u : k - 1;
+      ij[u] = idx[tc * k + j];
+      gj[u] = dg[tc * k + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tok && j0 + u < k && ij[u] == e) {
+        sel = j0 + u;
+        dgl = gj[u];
+      }
+  }
   float out;
   if (gating == 0) {
     const float mx = group_max<G>(l);
@@ -55,7 +74,7 @@ __global__ __launch_bounds__(256) void gating_bwd_kernel(const float* __restrict
     const float s = group_sum<G>(g * dgl);
     out = sel >= 0 ? g * (dgl - s) : 0.0f;
   }
-  if (valid) dl[t * E + e] = dl_add ? out + dl_add[t * E + e] : out;
+  if (valid) dl[t * E + e] = dl_add ? out + add : out;
 }
 
 template <int G>
