@@ -75,17 +75,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// LDS bytes of one compute unit
-constexpr int kLdsPerCu = 160 * 1024;
-
-// A workgroup barrier that orders LDS traffic only: outstanding global loads
-// stay in flight across it (a plain __syncthreads waits for them as well).
-__device__ __forceinline__ void lds_only_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

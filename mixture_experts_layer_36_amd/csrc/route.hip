@@ -23,6 +23,7 @@
 // give each token one lane.
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 #include <algorithm>
 #include <atomic>

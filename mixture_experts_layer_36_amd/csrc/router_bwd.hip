@@ -13,6 +13,7 @@
 //   summed in a fixed order.
 #include "common.h"
 #include "kernels.h"
+#include "stream.h"
 
 
 namespace moe {
