@@ -121,7 +121,9 @@ __device__ __forceinline__ float gelu_f(float z) {
 __device__ __forceinline__ float gelu_grad_f(float z) {
   return 0.5f * one_plus_erf(z * 0.70710678118654752f) + z * __expf(-0.5f * z * z) * 0.39894228040143268f;
 }
-__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
+// the hardware reciprocal (1 ulp) in place of a correctly rounded division,
+// whose scale / fix-up sequence the SwiGLU epilogues would run per element
+__device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // Row of accumulator element e (0..15) of a 32x32 MFMA block for this lane
 // (the lane holds column lane % 32).
