@@ -185,8 +185,8 @@ __device__ __forceinline__ void store_cols(T* p, const float (&v)[CPT]) {
   if constexpr (CPT * sizeof(T) == 16) {
     st16(p, pack16<T>(v));
   } else if constexpr (CPT * sizeof(T) == 8 && sizeof(T) == 2) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
-                                         bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]),
+                                         pack_bf16x2(v[2], v[3])};
   } else {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) p[c] = from_f32<T>(v[c]);

@@ -55,11 +55,19 @@ __device__ __forceinline__ unsigned bf16_bits(float f) {
   bf16 b = (bf16)f;
   return (unsigned)__builtin_bit_cast(unsigned short, b);
 }
+// two floats rounded to bf16 (to nearest even, as a single conversion does),
+// a in the low half: one v_cvt_pk_bf16_f32 instead of two conversions, a
+// shift and an or
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 template <>
 __device__ __forceinline__ u32x4 pack16<bf16>(const float* in) {
   u32x4 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = bf16_bits(in[2 * i]) | (bf16_bits(in[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
   return v;
 }
 

@@ -362,7 +362,7 @@ struct StagedTile {
     lds_char* p = base + r * ROWB + (((byte >> 4) ^ (r & 15)) << 4) + (byte & 15);
     if constexpr (sizeof(T) == 2)
       *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(p) =
-          u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     else
       *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
   }

@@ -259,8 +259,8 @@ template <> struct Run4<bf16> {
   }
   static __device__ __forceinline__ void load(const bf16* p, float (&v)[4]) { unpack(load_raw(p), v); }
   static __device__ __forceinline__ void store(bf16* p, const float (&v)[4]) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
-                                         bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]),
+                                         pack_bf16x2(v[2], v[3])};
   }
 };
 template <> struct Run4<float> {
