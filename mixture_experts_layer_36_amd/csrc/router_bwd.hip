@@ -440,10 +440,15 @@ __global__ __launch_bounds__(64 * NW) void router_wgrad_bf16mfma_kernel(const bf
       }
 }
 
-// Workgroups of the bf16 kernel that fit on one compute unit (LDS bound).
+// Workgroups of the bf16 kernel that fit on one compute unit at once (its
+// registers and LDS; asked once per instantiation).
 template <int EP, int NW>
-constexpr int rwb_per_cu() {
-  return kLdsPerCu / RwbShape<EP, NW>::LDS;
+static hipError_t rwb_per_cu(int* per_cu) {
+  static int n = 0;
+  static const hipError_t occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &n, reinterpret_cast<const void*>(router_wgrad_bf16mfma_kernel<EP, NW>), 64 * NW, 0);
+  *per_cu = n > 0 ? n : 1;
+  return occ;
 }
 
 template <int EP, int NW>
@@ -474,9 +479,17 @@ static hipError_t launch_rwg_bf16mfma(const RouteBwdArgs& a, hipStream_t st) {
     int64_t nb = ((int64_t)cus * per_cu + cb - 1) / cb;
     return (int)(nb < 1 ? 1 : nb > nbmax ? nbmax : nb);
   };
-  if ((a.d + 511) / 512 * nbmax >= cus) return launch_rwg_bf16mfma_nw<EP, 8>(a, blocks(512, rwb_per_cu<EP, 8>()), st);
-  if ((a.d + 255) / 256 * nbmax >= cus) return launch_rwg_bf16mfma_nw<EP, 4>(a, blocks(256, rwb_per_cu<EP, 4>()), st);
-  return launch_rwg_bf16mfma_nw<EP, 2>(a, blocks(128, rwb_per_cu<EP, 2>()), st);
+  int per_cu = 1;
+  if ((a.d + 511) / 512 * nbmax >= cus) {
+    if ((err = rwb_per_cu<EP, 8>(&per_cu)) != hipSuccess) return err;
+    return launch_rwg_bf16mfma_nw<EP, 8>(a, blocks(512, per_cu), st);
+  }
+  if ((a.d + 255) / 256 * nbmax >= cus) {
+    if ((err = rwb_per_cu<EP, 4>(&per_cu)) != hipSuccess) return err;
+    return launch_rwg_bf16mfma_nw<EP, 4>(a, blocks(256, per_cu), st);
+  }
+  if ((err = rwb_per_cu<EP, 2>(&per_cu)) != hipSuccess) return err;
+  return launch_rwg_bf16mfma_nw<EP, 2>(a, blocks(128, per_cu), st);
 }
 
 // bf16 x: the bf16 MFMA kernel with dlogits as hi + lo, E padded to 16, 32
