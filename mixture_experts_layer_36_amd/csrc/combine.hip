@@ -350,6 +350,23 @@ __global__ __launch_bounds__(256) void dispatch_bwd_mfma_kernel(const bf16* __re
       ad[u] = aok ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // the router term's operands (dlogits of token t0 + n, experts e .. e+7,
+  // and W_r[ic + b][e .. e+7] of every 32-expert block) are loaded before
+  // the first gathers, so that the MFMAs wait for them alone (the load
+  // counter is in order): the gathers stay in flight while they multiply.
+  // Loads are unconditional, from valid addresses; zeros are selected at use.
+  const int64_t ta = t0 + n < Tn ? t0 + n : Tn - 1;
+  u32x4 dlv[EK][2], wv[EK][8];
+#pragma unroll
+  for (int ek = 0; ek < EK; ++ek) {
+    const int e = 32 * ek + 8 * kg;
+    const bool e_ok = e < E;  // E is a multiple of 8: a lane's 8 experts are all in or all out
+    const float* dp = dl + ta * E + (e_ok ? e : 0);
+    dlv[ek][0] = ld16(dp);
+    dlv[ek][1] = ld16(dp + 4);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) wv[ek][b] = ld16(w_r + (int64_t)(col_ok ? ic + b : 0) * E + (e_ok ? e : 0));
+  }
   gather(0);  // in flight while the router term multiplies
 
   f32x4 acc[8];
@@ -358,11 +375,9 @@ __global__ __launch_bounds__(256) void dispatch_bwd_mfma_kernel(const bf16* __re
 #pragma unroll
   for (int ek = 0; ek < EK; ++ek) {
     const int e = 32 * ek + 8 * kg;
-    const bool e_ok = e < E;  // E is a multiple of 8: a lane's 8 experts are all in or all out
-    // A: dlogits of token t0 + n, experts e .. e+7, as hi + lo
-    const int64_t ta = t0 + n < Tn ? t0 + n : Tn - 1;
-    const float* dp = dl + ta * E + (e_ok ? e : 0);
-    const u32x4 d0 = ld16(dp), d1 = ld16(dp + 4);
+    const bool e_ok = e < E;
+    // A: dlogits as hi + lo
+    const u32x4 d0 = dlv[ek][0], d1 = dlv[ek][1];
     const bool a_ok = e_ok && t0 + n < Tn;
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -376,16 +391,11 @@ __global__ __launch_bounds__(256) void dispatch_bwd_mfma_kernel(const bf16* __re
     }
     const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, u32x4{hi[0], hi[1], hi[2], hi[3]});
     const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    // B: router weights W_r[ic + b][e .. e+7], 16 bytes per block
-    u32x4 wv[8];
+    // B: router weights, 16 bytes per block
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const u32x4 v = ld16(w_r + (int64_t)(col_ok ? ic + b : 0) * E + (e_ok ? e : 0));
-      wv[b] = (col_ok && e_ok) ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv[b]);
+      const bf16x8_t bw =
+          __builtin_bit_cast(bf16x8_t, (col_ok && e_ok) ? wv[ek][b] : u32x4{0u, 0u, 0u, 0u});
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[b], 0, 0, 0);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[b], 0, 0, 0);
     }
