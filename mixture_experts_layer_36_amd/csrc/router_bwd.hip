@@ -97,10 +97,10 @@ constexpr int kRwgWaves = 4;
 // value per lane, with no transposition.  A lane loads 16 bytes of x (V
 // consecutive columns c0 + V m + j of token t = 4-group base + lane / 16) and
 // feeds value j to the MFMA of column block j: block j's row m is column
-// c0 + V m + j, so one workgroup covers CW = 16 V columns.  The products are
-// exact in fp32 and summed in fp32 in a fixed order, as before; the 4 waves
-// take consecutive quarters of the block's tokens (4 token groups per round,
-// loads first) and their accumulators are summed in a fixed tree through LDS.
+// c0 + V m + j, so one workgroup covers CW = 16 V columns.  Products and
+// sums are fp32, in a fixed order: the 4 waves take consecutive quarters of
+// the block's tokens (4 token groups per round, loads first) and their
+// accumulators are summed in a fixed tree through LDS.
 template <typename T, int EP>
 __global__ __launch_bounds__(64 * kRwgWaves) void router_wgrad_mfma_kernel(const T* __restrict__ x,
                                                                            const float* __restrict__ dl,
