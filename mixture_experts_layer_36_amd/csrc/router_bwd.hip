@@ -271,8 +271,8 @@ static hipError_t launch_rwg_mfma(const RouteBwdArgs& a, hipStream_t st) {
 // columns of K row j / 4 of a 4 x 16 block and lane i receives column i's 4 K
 // values, so two reads give a lane the 8 consecutive tokens of its MFMA
 // operand.  A workgroup of NW waves owns 64 NW columns (64 per wave) for all
-// experts and tb tokens, so every token contributes a row run of 128 NW
-// bytes.  Two register sets hold the global loads of the next two steps:
+// experts and every gridDim.y-th 32-token step, so every token contributes a
+// row run of 128 NW bytes.  Two register sets hold the global loads of the next two steps:
 // step s + 2 is issued right after step s is in LDS, and the barriers order
 // LDS traffic only, so those loads stay in flight across them.  Two LDS
 // buffers, one barrier per step: a buffer is rewritten only after every wave
@@ -295,7 +295,7 @@ template <int EP, int NW>
 __global__ __launch_bounds__(64 * NW) void router_wgrad_bf16mfma_kernel(const bf16* __restrict__ x,
                                                                        const float* __restrict__ dl,
                                                                        float* __restrict__ partial, int64_t Tn, int d,
-                                                                       int E, int tb) {
+                                                                       int E) {
   using S = RwbShape<EP, NW>;
   constexpr int NB = EP / 16, CPR = S::CPR, XP = S::XP, DP = S::DP, XB = S::XB, DB = S::DB, BUF = S::BUF;
   constexpr int DQ = S::DQ, DR = S::DR, DPASS = S::DPASS;
@@ -304,9 +304,15 @@ __global__ __launch_bounds__(64 * NW) void router_wgrad_bf16mfma_kernel(const bf
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = blockIdx.x * S::COLS;
   const bool dthr = tid / DQ < DR;
-  const int64_t tbeg = (int64_t)blockIdx.y * tb;
-  const int64_t tend = tbeg + tb < Tn ? tbeg + tb : Tn;
-  const int nsteps = tend > tbeg ? (int)((tend - tbeg + 31) / 32) : 0;
+  // this workgroup's 32-token steps: global steps blockIdx.y + s gridDim.y,
+  // so that the workgroups of a column block read neighbouring tokens at any
+  // one time (contiguous blocks of tokens, 2 MB apart on the Mixtral shape,
+  // put every workgroup's reads on the same memory channels: 40 against 29
+  // us for the route backward, warm)
+  const int64_t gsteps = (Tn + 31) / 32;
+  const int nbk = (int)gridDim.y;
+  const int nsteps = blockIdx.y < gsteps ? (int)((gsteps - blockIdx.y + nbk - 1) / nbk) : 0;
+  const int64_t tfirst = 32 * (int64_t)blockIdx.y;  // a valid row for the loads past the end
 
   // global -> registers for one step: x rows tid / CPR + 8 p, 16-byte chunk
   // tid % CPR; dlogits rows tid / DQ + DR p, experts 4 (tid % DQ) .. + 3.
@@ -317,30 +323,30 @@ __global__ __launch_bounds__(64 * NW) void router_wgrad_bf16mfma_kernel(const bf
   const bool xcol_ok = xcol < d;  // d is a multiple of 8: a chunk is all in or all out
   const int de = 4 * (tid % DQ);
   auto gload = [&](int s, u32x4 (&xr)[4], float (&dv)[DPASS][4]) {
-    const int64_t t0 = tbeg + 32 * s;
+    const int64_t t0 = 32 * ((int64_t)blockIdx.y + (int64_t)s * nbk);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int64_t t = t0 + tid / CPR + 8 * p;
-      xr[p] = ld16(x + (t < tend ? t : tbeg) * d + (xcol_ok ? xcol : 0));
+      xr[p] = ld16(x + (t < Tn ? t : tfirst) * d + (xcol_ok ? xcol : 0));
     }
 #pragma unroll
     for (int p = 0; p < DPASS; ++p) {
       const int64_t t = t0 + tid / DQ + DR * p;
-      const int64_t tc = t < tend ? t : tbeg;
+      const int64_t tc = t < Tn ? t : tfirst;
 #pragma unroll
       for (int q = 0; q < 4; ++q) dv[p][q] = dl[tc * E + (de + q < E ? de + q : 0)];
     }
   };
   auto lwrite = [&](char* buf, int s, const u32x4 (&xr)[4], const float (&dv)[DPASS][4]) {
-    const int64_t t0 = tbeg + 32 * s;
+    const int64_t t0 = 32 * ((int64_t)blockIdx.y + (int64_t)s * nbk);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const bool ok = xcol_ok && t0 + tid / CPR + 8 * p < tend;
+      const bool ok = xcol_ok && t0 + tid / CPR + 8 * p < Tn;
       st16(buf + (tid / CPR + 8 * p) * XP + (tid % CPR) * 16, ok ? xr[p] : u32x4{0u, 0u, 0u, 0u});
     }
 #pragma unroll
     for (int p = 0; p < DPASS; ++p) {
-      const bool tok = t0 + tid / DQ + DR * p < tend;
+      const bool tok = t0 + tid / DQ + DR * p < Tn;
       uint32_t h[4], l[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -454,12 +460,11 @@ static hipError_t rwb_per_cu(int* per_cu) {
 template <int EP, int NW>
 static hipError_t launch_rwg_bf16mfma_nw(const RouteBwdArgs& a, int nb, hipStream_t st) {
   using S = RwbShape<EP, NW>;
-  const int64_t tb0 = (a.T + nb - 1) / nb;
-  const int tb = (int)((tb0 + 31) / 32 * 32);   // tokens per block, whole steps
-  const int nbr = (int)((a.T + tb - 1) / tb);  // blocks that hold tokens
+  const int64_t gsteps = (a.T + 31) / 32;
+  const int nbr = (int)(nb < gsteps ? nb : gsteps);  // token blocks, each with at least one step
   const dim3 grid((unsigned)((a.d + S::COLS - 1) / S::COLS), nbr);
   hipLaunchKernelGGL((router_wgrad_bf16mfma_kernel<EP, NW>), grid, dim3(S::NT), 0, st, (const bf16*)a.x, a.dlogits,
-                     a.partial, a.T, (int)a.d, a.E, tb);
+                     a.partial, a.T, (int)a.d, a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_rwg_reduce<bf16>(a, nbr, st);
