@@ -168,34 +168,43 @@ __device__ __forceinline__ bool row_tile_of(const gemm::Args& a, int& g, int64_t
   return false;
 }
 
-// 1 + erf(x), from erfc of |x|: erfc(u) = t exp(-u^2 + P(t)) with t = 1 / (1
-// + u / 2) and P the degree-9 Chebyshev fit published with this form in
+// Phi(z) = (1 + erf(z / sqrt 2)) / 2, the normal distribution function, from
+// erfc of u = |z| / sqrt 2: erfc(u) = t exp(-u^2 + P(t)) with t = 1 / (1 +
+// u / 2) and P the degree-9 Chebyshev fit published with this form in
 // Numerical Recipes (Press, Teukolsky, Vetterling and Flannery, 2nd ed.,
 // section 6.2), whose fractional error stays below 1.2e-7 for every u >= 0.
-// For x < 0 the result is erfc(|x|) itself, free of the cancellation in 1 +
-// erf(x).  One reciprocal, one exponential and nine FMAs, without the range
+// Written in z for the hardware 2^x: the exponent is log2(e) (P(t) - u^2) - 1
+// (the -1 takes the halving), with log2(e) folded into P's coefficients, and
+// w = log2(e) z^2 / 2 is returned for GELU', whose Gaussian term is 2^-w.
+// For z < 0 the result is erfc itself, free of the cancellation in 1 + erf.
+// One reciprocal, one exponential and eleven multiply-adds, without the range
 // branches of a general erff: the GELU epilogues run it once per element.
-__device__ __forceinline__ float one_plus_erf(float x) {
-  const float u = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, u, 1.0f));
-  float p = 0.17087277f;
-  p = fmaf(p, t, -0.82215223f);
-  p = fmaf(p, t, 1.48851587f);
-  p = fmaf(p, t, -1.13520398f);
-  p = fmaf(p, t, 0.27886807f);
-  p = fmaf(p, t, -0.18628806f);
-  p = fmaf(p, t, 0.09678418f);
-  p = fmaf(p, t, 0.37409196f);
-  p = fmaf(p, t, 1.00002368f);
-  p = fmaf(p, t, -1.26551223f);
-  const float q = t * __expf(fmaf(-u, u, p));
-  return x >= 0.0f ? 2.0f - q : q;
+__device__ __forceinline__ float phi_f(float z, float& w) {
+  constexpr float kL2e = 1.4426950408889634f;
+  const float a = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.35355339059327373f, a, 1.0f));  // 1 / (1 + u / 2)
+  float p = 0.17087277f * kL2e;
+  p = fmaf(p, t, -0.82215223f * kL2e);
+  p = fmaf(p, t, 1.48851587f * kL2e);
+  p = fmaf(p, t, -1.13520398f * kL2e);
+  p = fmaf(p, t, 0.27886807f * kL2e);
+  p = fmaf(p, t, -0.18628806f * kL2e);
+  p = fmaf(p, t, 0.09678418f * kL2e);
+  p = fmaf(p, t, 0.37409196f * kL2e);
+  p = fmaf(p, t, 1.00002368f * kL2e);
+  p = fmaf(p, t, -1.26551223f * kL2e - 1.0f);
+  w = (0.5f * kL2e * z) * z;
+  const float h = t * __builtin_amdgcn_exp2f(p - w);  // erfc(u) / 2
+  return z >= 0.0f ? 1.0f - h : h;
 }
 __device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * one_plus_erf(z * 0.70710678118654752f);
+  float w;
+  return z * phi_f(z, w);
 }
 __device__ __forceinline__ float gelu_grad_f(float z) {
-  return 0.5f * one_plus_erf(z * 0.70710678118654752f) + z * __expf(-0.5f * z * z) * 0.39894228040143268f;
+  float w;
+  const float ph = phi_f(z, w);
+  return fmaf(z * 0.3989422804014327f, __builtin_amdgcn_exp2f(-w), ph);  // Phi(z) + z exp(-z^2 / 2) / sqrt(2 pi)
 }
 // the hardware reciprocal (1 ulp) in place of a correctly rounded division,
 // whose scale / fix-up sequence the SwiGLU epilogues would run per element
