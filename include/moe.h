@@ -217,8 +217,13 @@ int moe_dispatch_noalloc(const moe_config* cfg, const void* x,
  *   x_rows [rows_max, d]; weights per expert:
  *     GELU:   w_in = W1 [E', d, ffn], w_out = W2 [E', ffn, d], w_up NULL;
  *     SwiGLU: w_in = W_gate, w_up = W_up [E', d, ffn], w_out = W_down.
- *   act_saved: GELU Z = x W1 [rows_max, ffn]; SwiGLU [rows_max, 2*ffn] with
- *     A = x W_gate in columns [0, ffn) and B = x W_up in [ffn, 2*ffn).
+ *   act_saved: what the backward multiplies dL/dh by (the derivatives of
+ *     the activation at this forward's pre-activations, so that
+ *     moe_expert_ffn_bwd does not evaluate the activation again):
+ *     GELU [rows_max, ffn]: GELU'(Z) = Phi(Z) + Z phi(Z) with Z = x W1;
+ *     SwiGLU [rows_max, 2*ffn]: dh/dA = B s (1 + A (1 - s)) in columns
+ *     [0, ffn) and dh/dB = silu(A) in [ffn, 2*ffn), with A = x W_gate,
+ *     B = x W_up, s = sigmoid(A).  Rounded to dtype like the other outputs.
  *   h [rows_max, ffn]: GELU(Z) (exact erf form) or silu(A) * B.
  *   y_rows [rows_max, d]: h W_out.  Rows outside the segments are untouched. */
 int moe_expert_ffn_fwd(const moe_config* cfg, const moe_groups* grp,

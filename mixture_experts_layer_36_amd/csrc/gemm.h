@@ -9,10 +9,10 @@ namespace gemm {
 enum { KIND_FWD = 0, KIND_DGRAD = 1 };
 enum {
   EPI_STORE = 0,         // C = acc
-  EPI_GELU_FWD = 1,      // C = Z = acc, C2 = GELU(Z)
-  EPI_SWIGLU_FWD = 2,    // tile pairs gate|up columns: C[:, f] = A, C[:, c_split+f] = B, C2 = silu(A)*B
-  EPI_GELU_BWD = 3,      // C = acc * GELU'(X1)
-  EPI_SWIGLU_BWD = 4,    // X1 = [A|B]; C[:, f] = dA, C[:, c_split+f] = dB with dH = acc
+  EPI_GELU_FWD = 1,      // Z = acc: C = GELU'(Z), C2 = GELU(Z)
+  EPI_SWIGLU_FWD = 2,    // tile pairs gate|up columns A|B: C[:, f] = dH/dA, C[:, c_split+f] = dH/dB, C2 = H = silu(A)*B
+  EPI_GELU_BWD = 3,      // X1 = GELU'(Z): C = acc * X1
+  EPI_SWIGLU_BWD = 4,    // X1 = [dH/dA | dH/dB]; C[:, f] = dA, C[:, c_split+f] = dB with dH = acc
   EPI_STORE_SPLITN = 5,  // wgrad: columns >= c_split go to C2
   // fused forward (no saved activations; weighted, un-permuted output rows)
   EPI_STORE_SCATTER = 6, // C row scatter[r] = row_scale[scatter[r]] * acc of row r

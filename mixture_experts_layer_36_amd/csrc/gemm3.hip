@@ -381,9 +381,10 @@ struct StagedTile {
   }
 };
 
-// Row-split kernels: EPI_STORE (C), EPI_GELU_FWD (C = Z | C2 = GELU(Z)) and the
-// SwiGLU gate|up pair (C = A | B at column f and c_split + f, C2 = silu(A) B).
-// Variants of the fused forward: EPI_SWIGLU_FWD_H and EPI_GELU_FWD_H write
+// Row-split kernels: EPI_STORE (C), EPI_GELU_FWD (C = GELU'(Z) | C2 = GELU(Z))
+// and the SwiGLU gate|up pair (C = dH/dA | dH/dB at column f and c_split + f,
+// C2 = silu(A) B): the saved factors are those of gelu_fwd_save and
+// swiglu_fwd_save.  Variants of the fused forward: EPI_SWIGLU_FWD_H and EPI_GELU_FWD_H write
 // only the hidden activation (C2), EPI_STORE_SCATTER writes output row r to
 // row scatter[r] of C, scaled by row_scale[scatter[r]] before rounding.
 template <int FM, int FN, bool PAIR, int EPI>
@@ -392,9 +393,9 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
                                                      int64_t n0, int64_t N, char* smem) {
   static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
   constexpr bool GELU = EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_GELU_FWD_H;
-  constexpr bool SAVE = EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD;  // also Z or A | B
+  constexpr bool SAVE = EPI == gemm::EPI_GELU_FWD || EPI == gemm::EPI_SWIGLU_FWD;  // also the factors
   constexpr bool SCAT = EPI == gemm::EPI_STORE_SCATTER;
-  // staged columns: PAIR A | B | H or H; GELU Z | GELU(Z) or GELU(Z); else the output
+  // staged columns: PAIR D1 | D2 | H or H; GELU D | GELU(Z) or GELU(Z); else the output
   constexpr int SC = PAIR ? (SAVE ? 384 : 128) : (GELU && SAVE ? 512 : 256);
   constexpr int HOFF = PAIR ? (SAVE ? 256 : 0) : (SAVE ? 256 : 0);  // column of the hidden activation
   const StagedTile<bf16, SC> st{(lds_char*)smem};
@@ -414,16 +415,19 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
     for (int g = 0; g < 4; ++g) {
       const int tc = tacc_col(g, lane);
       if constexpr (PAIR) {
-        float av[4], bv[4], hv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          av[q] = acc[i][0][4 * g + q];
-          bv[q] = acc[i][1][4 * g + q];
-          hv[q] = av[q] * sigmoid_f(av[q]) * bv[q];
-        }
+        float hv[4];
         if constexpr (SAVE) {
-          st.put4(sr, bcol[0] + tc, av);
-          st.put4(sr, bcol[1] + tc, bv);
+          float d1[4], d2[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fwd_save(acc[i][0][4 * g + q], acc[i][1][4 * g + q], d1[q], d2[q]);
+          st.put4(sr, bcol[0] + tc, d1);
+          st.put4(sr, bcol[1] + tc, d2);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float av = acc[i][0][4 * g + q];
+            hv[q] = av * sigmoid_f(av) * acc[i][1][4 * g + q];
+          }
         }
         st.put4(sr, HOFF + bcol[0] + tc, hv);
       } else {
@@ -432,12 +436,19 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * scale;
-          if constexpr (!GELU || SAVE) st.put4(sr, bcol[j] + tc, v);
-          if constexpr (GELU) {
+          if constexpr (GELU && SAVE) {
+            float d[4], h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = gelu_fwd_save(v[q], d[q]);
+            st.put4(sr, bcol[j] + tc, d);
+            st.put4(sr, HOFF + bcol[j] + tc, h);
+          } else if constexpr (GELU) {
             float h[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
             st.put4(sr, HOFF + bcol[j] + tc, h);
+          } else {
+            st.put4(sr, bcol[j] + tc, v);
           }
         }
       }
@@ -464,9 +475,9 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
 }
 
 // Activation backward of the row-split DGRAD kernels, staged the same way:
-// dZ = acc * GELU'(Z) (X1 = Z), or for SwiGLU with X1 = [A | B]:
-// dA = acc * B * s * (1 + A (1 - s)), dB = acc * silu(A) (s = sigmoid(A)),
-// stored at columns n and c_split + n of C.  The accumulators are staged in
+// X1 holds the factors the forward saved, dZ = acc * GELU'(Z), or for SwiGLU
+// dA = acc * dH/dA and dB = acc * dH/dB from X1's columns n and c_split + n,
+// stored at the same columns of C.  The accumulators are staged in
 // fp32; a thread then takes 8 consecutive columns of a staged row, with all
 // its 16-byte loads of the saved activations for the pass issued before any
 // arithmetic, and stores 16 bytes per output.
@@ -512,7 +523,7 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = (int)threadIdx.x + 512 * u, r = q >> 5, c = (q & 31) * 2;  // two fp32 chunks
-      float g8[8], z[8];
+      float g8[8], d0[8];
       {
         const u32x4 lo = st.get(r, c), hi = st.get(r, c + 1);
 #pragma unroll
@@ -521,15 +532,14 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
           g8[4 + e] = __uint_as_float(hi[e]);
         }
       }
-      unpack16<bf16>(x0[u], z);
+      unpack16<bf16>(x0[u], d0);
       if constexpr (SW) {
-        float bv[8], da[8], db[8];
-        unpack16<bf16>(x1[u], bv);
+        float d1[8], da[8], db[8];
+        unpack16<bf16>(x1[u], d1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float sg = sigmoid_f(z[e]);
-          da[e] = g8[e] * bv[e] * sg * (1.0f + z[e] * (1.0f - sg));
-          db[e] = g8[e] * z[e] * sg;
+          da[e] = g8[e] * d0[e];
+          db[e] = g8[e] * d1[e];
         }
         if (ok[u]) {
           st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(da));
@@ -538,7 +548,7 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
       } else {
         float dz[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dz[e] = g8[e] * gelu_grad_f(z[e]);
+        for (int e = 0; e < 8; ++e) dz[e] = g8[e] * d0[e];
         if (ok[u]) st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(dz));
       }
     }

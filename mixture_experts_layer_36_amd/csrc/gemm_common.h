@@ -201,14 +201,29 @@ __device__ __forceinline__ float gelu_f(float z) {
   float w;
   return z * phi_f(z, w);
 }
-__device__ __forceinline__ float gelu_grad_f(float z) {
-  float w;
-  const float ph = phi_f(z, w);
-  return fmaf(z * 0.3989422804014327f, __builtin_amdgcn_exp2f(-w), ph);  // Phi(z) + z exp(-z^2 / 2) / sqrt(2 pi)
-}
 // the hardware reciprocal (1 ulp) in place of a correctly rounded division,
 // whose scale / fix-up sequence the SwiGLU epilogues would run per element
 __device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
+// Forward activations together with the factor that their backward
+// multiplies dL/dh by, which the forward saves in place of the
+// pre-activations: the backward epilogue is then one product per element
+// instead of a second evaluation of Phi or the sigmoid.
+//   GELU:   h = z Phi(z),   d = dh/dz = Phi(z) + z exp(-z^2 / 2) / sqrt(2 pi)
+//   SwiGLU: h = silu(a) b,  d1 = dh/da = b s (1 + a (1 - s)),  d2 = dh/db = silu(a)
+// with s = sigmoid(a); h is formed exactly as without the factors.
+__device__ __forceinline__ float gelu_fwd_save(float z, float& d) {
+  float w;
+  const float ph = phi_f(z, w);
+  d = fmaf(z * 0.3989422804014327f, __builtin_amdgcn_exp2f(-w), ph);
+  return z * ph;
+}
+__device__ __forceinline__ float swiglu_fwd_save(float a, float b, float& d1, float& d2) {
+  const float s = sigmoid_f(a);
+  d2 = a * s;
+  d1 = b * s * fmaf(a, 1.0f - s, 1.0f);
+  return d2 * b;
+}
 
 // Row of accumulator element e (0..15) of a 32x32 MFMA block for this lane
 // (the lane holds column lane % 32).
@@ -259,10 +274,11 @@ __device__ __forceinline__ void rows_epilogue(const gemm::Args& a, f32x16 (&acc)
         for (int e = 0; e < 16; ++e) {
           const int64_t rr = row_begin + wm0 + i * 32 + acc_row(e, lane);
           if (rr >= row_end) continue;
-          const float av = acc[i][j][e], bv = acc[i][j + FN / 2][e];
-          C[rr * a.ldc + f] = from_f32<T>(av);
-          C[rr * a.ldc + a.c_split + f] = from_f32<T>(bv);
-          C2[rr * a.ldc2 + f] = from_f32<T>(av * sigmoid_f(av) * bv);
+          float d1, d2;
+          const float hv = swiglu_fwd_save(acc[i][j][e], acc[i][j + FN / 2][e], d1, d2);
+          C[rr * a.ldc + f] = from_f32<T>(d1);
+          C[rr * a.ldc + a.c_split + f] = from_f32<T>(d2);
+          C2[rr * a.ldc2 + f] = from_f32<T>(hv);
         }
       }
   } else {
@@ -280,17 +296,15 @@ __device__ __forceinline__ void rows_epilogue(const gemm::Args& a, f32x16 (&acc)
           if constexpr (EPI == gemm::EPI_STORE) {
             C[rr * a.ldc + n] = from_f32<T>(v);
           } else if constexpr (EPI == gemm::EPI_GELU_FWD) {
-            C[rr * a.ldc + n] = from_f32<T>(v);
-            C2[rr * a.ldc2 + n] = from_f32<T>(gelu_f(v));
+            float dv;
+            const float hv = gelu_fwd_save(v, dv);
+            C[rr * a.ldc + n] = from_f32<T>(dv);
+            C2[rr * a.ldc2 + n] = from_f32<T>(hv);
           } else if constexpr (EPI == gemm::EPI_GELU_BWD) {
-            const float z = to_f32(X1[rr * a.ldx + n]);
-            C[rr * a.ldc + n] = from_f32<T>(v * gelu_grad_f(z));
+            C[rr * a.ldc + n] = from_f32<T>(v * to_f32(X1[rr * a.ldx + n]));
           } else if constexpr (EPI == gemm::EPI_SWIGLU_BWD) {
-            const float av = to_f32(X1[rr * a.ldx + n]);
-            const float bv = to_f32(X1[rr * a.ldx + a.c_split + n]);
-            const float s = sigmoid_f(av);
-            C[rr * a.ldc + n] = from_f32<T>(v * bv * s * (1.0f + av * (1.0f - s)));
-            C[rr * a.ldc + a.c_split + n] = from_f32<T>(v * av * s);
+            C[rr * a.ldc + n] = from_f32<T>(v * to_f32(X1[rr * a.ldx + n]));
+            C[rr * a.ldc + a.c_split + n] = from_f32<T>(v * to_f32(X1[rr * a.ldx + a.c_split + n]));
           }
         }
       }
@@ -388,15 +402,12 @@ __device__ __forceinline__ void rows_epilogue_t(const gemm::Args& a, f32x16 (&ac
         for (int g = 0; g < 4; ++g) {
           const int64_t f = n0 + bcol[j] + tacc_col(g, lane);
           if (f >= N) continue;
-          float av[4], bv[4], hv[4];
+          float d1[4], d2[4], hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            av[q] = acc[i][j][4 * g + q];
-            bv[q] = acc[i][j + FN / 2][4 * g + q];
-            hv[q] = av[q] * sigmoid_f(av[q]) * bv[q];
-          }
-          Run4<T>::store(C + rr * a.ldc + f, av);
-          Run4<T>::store(C + rr * a.ldc + a.c_split + f, bv);
+          for (int q = 0; q < 4; ++q)
+            hv[q] = swiglu_fwd_save(acc[i][j][4 * g + q], acc[i][j + FN / 2][4 * g + q], d1[q], d2[q]);
+          Run4<T>::store(C + rr * a.ldc + f, d1);
+          Run4<T>::store(C + rr * a.ldc + a.c_split + f, d2);
           Run4<T>::store(C2 + rr * a.ldc2 + f, hv);
         }
     } else {
@@ -412,10 +423,10 @@ __device__ __forceinline__ void rows_epilogue_t(const gemm::Args& a, f32x16 (&ac
           if constexpr (EPI == gemm::EPI_STORE) {
             Run4<T>::store(C + rr * a.ldc + n, v);
           } else if constexpr (EPI == gemm::EPI_GELU_FWD) {
-            float h[4];
+            float dv[4], h[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
-            Run4<T>::store(C + rr * a.ldc + n, v);
+            for (int q = 0; q < 4; ++q) h[q] = gelu_fwd_save(v[q], dv[q]);
+            Run4<T>::store(C + rr * a.ldc + n, dv);
             Run4<T>::store(C2 + rr * a.ldc2 + n, h);
           }
         }
@@ -423,7 +434,8 @@ __device__ __forceinline__ void rows_epilogue_t(const gemm::Args& a, f32x16 (&ac
   }
 }
 
-// The backward activations read X1 (Z, or A | B).  Each lane's loads of one
+// The backward activations read X1 (the saved factor dh/dz, or dh/da | dh/db)
+// and multiply the accumulators by it.  Each lane's loads of one
 // 32-row block (FN x 4 runs, two per run for SwiGLU) are issued together and
 // one block ahead of the arithmetic; they are unconditional, from the tile's
 // first row / column when the run is out of range, and only the stores are
@@ -470,10 +482,8 @@ __device__ __forceinline__ void rows_epilogue_t_bwd(const gemm::Args& a, f32x16 
           float da[4], db[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float v = acc[i][j][4 * g + q], av = x0[q], bv = x1[q];
-            const float sg = sigmoid_f(av);
-            da[q] = v * bv * sg * (1.0f + av * (1.0f - sg));
-            db[q] = v * av * sg;
+            da[q] = acc[i][j][4 * g + q] * x0[q];
+            db[q] = acc[i][j][4 * g + q] * x1[q];
           }
           if (row_ok && n < N) {
             Run4<T>::store(C + rr * a.ldc + n, da);
@@ -482,7 +492,7 @@ __device__ __forceinline__ void rows_epilogue_t_bwd(const gemm::Args& a, f32x16 
         } else {
           float dz[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) dz[q] = acc[i][j][4 * g + q] * gelu_grad_f(x0[q]);
+          for (int q = 0; q < 4; ++q) dz[q] = acc[i][j][4 * g + q] * x0[q];
           if (row_ok && n < N) Run4<T>::store(C + rr * a.ldc + n, dz);
         }
       }

@@ -56,7 +56,7 @@ int check_config(const moe_config* c) {
   if (c->T * c->k >= (int64_t)1 << 31 || c->T >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (c->d >= (int64_t)1 << 24 || c->ffn >= (int64_t)1 << 24) return MOE_ERR_UNSUPPORTED;
   // every buffer resource of the expert GEMMs spans at most 256 rows of one
-  // operand, so one row (x: d elements; [A | B]: 2 ffn; the shared experts:
+  // operand, so one row (x: d elements; the saved SwiGLU factors: 2 ffn; the shared experts:
   // 2 n_shared ffn_shared) must stay within kMaxRowBytes for its extent to fit
   const int64_t s = c->dtype == MOE_BF16 ? 2 : 4;
   const int64_t m = c->act == MOE_ACT_SWIGLU ? 2 : 1;

@@ -279,6 +279,27 @@ def expert_ffn_backward(xp, do, w_in, w_out, act: str, w_up=None) -> dict:
     return out
 
 
+def activation_factors(fwd: dict, act: str) -> dict:
+    """Partial derivatives of the activation h at a forward's
+    pre-activations (the factors of the chain rule in [EPDP] 三.3 that take
+    dL/dh to dL/dz, or to dL/da and dL/db):
+
+    gelu:   d  = dh/dz = GELU'(z)
+    swiglu: d1 = dh/da = b * s * (1 + a (1 - s)),  s = sigmoid(a)
+            d2 = dh/db = silu(a)
+    so that dz = dh * d, da = dh * d1, db = dh * d2 as in
+    expert_ffn_backward.  A forward may keep these in place of z or a, b
+    when h itself is saved.
+    """
+    if act == "gelu":
+        return {"d": gelu_grad(fwd["z"])}
+    if act == "swiglu":
+        a, b = fwd["a"], fwd["b"]
+        s = sigmoid(a)
+        return {"d1": b * s * (1.0 + a * (1.0 - s)), "d2": silu(a)}
+    raise ValueError(act)
+
+
 # --------------------------------------------------------------------------
 # combine  [EP 二 step 4; PP 三 outputs merged]
 # --------------------------------------------------------------------------

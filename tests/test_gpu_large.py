@@ -4,7 +4,8 @@ The Mixtral-shaped (T 16384, d 4096, ffn 14336, 8 experts, top-2, SwiGLU)
 and DeepSeek-V2-Lite-shaped (T 16384, d 2048, ffn 1408, 64 experts, top-6,
 2 shared experts) steps are compared with the float64 oracle element by
 element on every output: logits, routing and layout (bit for bit), gate
-weights, the saved activations A | B, h, y_perm, dx_perm, y, d_topk_w,
+weights, the saved activation derivatives dh/dA | dh/dB, h, y_perm,
+dx_perm, y, d_topk_w,
 dlogits, dW_r, every expert weight gradient, the shared experts' weight
 gradients and dx.
 
@@ -103,12 +104,13 @@ class PerExpertParity:
         errs = {}
         if r1 > r0:
             act = host(L.act_saved[r0:r1])
+            fac = oracle.activation_factors(fw, wl.act)
             if swiglu:
-                errs["A"] = assert_close(f"A[e{e}]", act[:, :F], fw["a"], tol)
-                errs["B"] = assert_close(f"B[e{e}]", act[:, F:], fw["b"], tol)
+                errs["dh/da"] = assert_close(f"dh/da[e{e}]", act[:, :F], fac["d1"], tol)
+                errs["dh/db"] = assert_close(f"dh/db[e{e}]", act[:, F:], fac["d2"], tol)
             else:
-                errs["Z"] = assert_close(f"Z[e{e}]", act, fw["z"], tol)
-            del act
+                errs["dh/dz"] = assert_close(f"dh/dz[e{e}]", act, fac["d"], tol)
+            del act, fac
             errs["h"] = assert_close(f"h[e{e}]", host(L.h[r0:r1]), fw["h"], tol)
             errs["y_perm"] = assert_close(f"y_perm[e{e}]", host(L.y_perm[r0:r1]), fw["o"], tol)
             errs["dy_perm"] = assert_close(f"dy_perm[e{e}]", host(L.dy_perm[r0:r1]), do, tol)

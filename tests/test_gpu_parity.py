@@ -292,18 +292,19 @@ def test_ffn_caller_group_table_of_65():
     xf, dyf = oracle.to_f64(x), oracle.to_f64(dy)
     Wi, Wu, Wo = oracle.to_f64(w_in), oracle.to_f64(w_up), oracle.to_f64(w_out)
     n = int(off[-1])
-    ref = {k: np.zeros(s) for k, s in (("a", (n, F)), ("b", (n, F)), ("h", (n, F)), ("y", (n, d)),
+    ref = {k: np.zeros(s) for k, s in (("d1", (n, F)), ("d2", (n, F)), ("h", (n, F)), ("y", (n, d)),
                                         ("dx", (n, d)), ("dwi", (G, d, F)), ("dwu", (G, d, F)),
                                         ("dwo", (G, F, d)))}
     for g in range(G):
         r0, r1 = int(off[g]), int(off[g + 1])
         fw = oracle.expert_ffn_forward(xf[r0:r1], Wi[g], Wo[g], "swiglu", Wu[g])
         bw = oracle.expert_ffn_backward(xf[r0:r1], dyf[r0:r1], Wi[g], Wo[g], "swiglu", Wu[g])
-        ref["a"][r0:r1], ref["b"][r0:r1], ref["h"][r0:r1], ref["y"][r0:r1] = fw["a"], fw["b"], fw["h"], fw["o"]
+        fac = oracle.activation_factors(fw, "swiglu")
+        ref["d1"][r0:r1], ref["d2"][r0:r1], ref["h"][r0:r1], ref["y"][r0:r1] = fac["d1"], fac["d2"], fw["h"], fw["o"]
         ref["dx"][r0:r1] = bw["dxp"]
         ref["dwi"][g], ref["dwu"][g], ref["dwo"][g] = bw["dw_in"], bw["dw_up"], bw["dw_out"]
     got_act = host(act)[:n]
-    got = {"a": got_act[:, :F], "b": got_act[:, F:], "h": host(h)[:n], "y": host(y)[:n], "dx": host(dx)[:n],
+    got = {"d1": got_act[:, :F], "d2": got_act[:, F:], "h": host(h)[:n], "y": host(y)[:n], "dx": host(dx)[:n],
            "dwi": host(dwi), "dwu": host(dwu), "dwo": host(dwo)}
     errs = {}
     for k in ref:

@@ -56,6 +56,39 @@ def test_activation_values():
     assert abs(oracle.gelu(np.array(10.0)) - 10.0) < 1e-12
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_activation_factors(act):
+    """The factors a forward may save for the backward are the elementwise
+    partial derivatives of h: torch CPU autograd of the same activation, and
+    central differences of the oracle's forward in its pre-activations
+    (x = I, so z = W1, a = W_gate, b = W_up; h is elementwise in them, so one
+    shift of every entry gives every derivative)."""
+    rng = np.random.default_rng(5)
+    n, F = 6, 7
+    w_in = rng.normal(size=(n, F)) * 2.0
+    w_up = rng.normal(size=(n, F)) * 2.0 if act == "swiglu" else None
+    w_out, eye = np.eye(F), np.eye(n)
+    f = oracle.activation_factors(oracle.expert_ffn_forward(eye, w_in, w_out, act, w_up), act)
+    a = torch.tensor(w_in, requires_grad=True)
+    if act == "gelu":
+        torch.nn.functional.gelu(a).sum().backward()
+        np.testing.assert_allclose(f["d"], a.grad.numpy(), rtol=1e-12, atol=1e-14)
+    else:
+        b = torch.tensor(w_up, requires_grad=True)
+        (torch.nn.functional.silu(a) * b).sum().backward()
+        np.testing.assert_allclose(f["d1"], a.grad.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(f["d2"], b.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+    def h_at(wi, wu):
+        return oracle.expert_ffn_forward(eye, wi, w_out, act, wu)["h"]
+    eps = 1e-6
+    fd = (h_at(w_in + eps, w_up) - h_at(w_in - eps, w_up)) / (2 * eps)
+    np.testing.assert_allclose(f["d"] if act == "gelu" else f["d1"], fd, rtol=1e-6, atol=1e-8)
+    if act == "swiglu":
+        fd = (h_at(w_in, w_up + eps) - h_at(w_in, w_up - eps)) / (2 * eps)
+        np.testing.assert_allclose(f["d2"], fd, rtol=1e-6, atol=1e-8)
+
+
 # ---------------------------------------------------------------- dense references
 def brute_route(lg, k, C):
     """Top-k by subset enumeration + sequential capacity counters ->
