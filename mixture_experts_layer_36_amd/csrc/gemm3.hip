@@ -31,6 +31,8 @@
 // The B fragment is the MFMA's first operand, so the accumulators hold C^T
 // blocks: a lane owns one row of C and runs of 4 consecutive columns, which
 // the epilogues store (and the backward activations load) 8 bytes at a time.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 #include "gemm_common.h"
@@ -373,13 +375,55 @@ struct StagedTile {
   // to dst(staged row, element column of the chunk, data)
   template <int NT, typename Dst>
   __device__ __forceinline__ void store_all(const Dst& dst) const {
+    static_assert(ROWS * CH % NT == 0, "every thread takes the same number of chunks");
 #pragma unroll
-    for (int q = (int)threadIdx.x; q < ROWS * CH; q += NT) {
-      const int r = q / CH, c = q - r * CH;
+    for (int j = 0; j < ROWS * CH / NT; ++j) {
+      const int q = (int)threadIdx.x + NT * j, r = q / CH, c = q - r * CH;
       dst(r, c * (16 / (int)sizeof(T)), get(r, c));
     }
   }
+  // the chunks of column part P of PARTS equal parts of the table, handed to
+  // dst(staged row, element column within the part, data): one destination
+  // per call, so no thread selects between outputs
+  template <int NT, int PARTS, int P, typename Dst>
+  __device__ __forceinline__ void store_part(const Dst& dst) const {
+    constexpr int CP = CH / PARTS;
+    static_assert(CH % PARTS == 0 && ROWS * CP % NT == 0, "every thread takes the same number of chunks");
+#pragma unroll
+    for (int j = 0; j < ROWS * CP / NT; ++j) {
+      const int q = (int)threadIdx.x + NT * j, r = q / CP, c = q - r * CP;
+      dst(r, c * (16 / (int)sizeof(T)), get(r, P * CP + c));
+    }
+  }
 };
+
+// Stores of a tile go to a uniform base (the tile's first row and column)
+// plus a 32-bit element offset.  Tile rows are below 256 and every leading
+// dimension below 2^22 elements (the entry points reject rows wider than
+// 8 MiB), so row * ld + column stays below 2^31 and both factors fit the
+// 24-bit multiplier, which issues at the full rate, where the 32-bit and
+// 64-bit products of a 64-bit row * ld per 16-byte store take four slots
+// each.
+__device__ __forceinline__ uint32_t tile_off(int tr, uint32_t ld, int c) {
+  return __umul24((uint32_t)tr, ld) + (uint32_t)c;
+}
+// f(I) for I = 0 .. N-1 with I a compile-time constant: straight-line code
+// that no loop pass has to unroll.  (The forward epilogue's pass loop, whose
+// store branches depend only on the thread, was unswitched on them and then
+// left rolled, with the accumulators indexed at run time from scratch memory.)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// rows (or columns) of a tile that exist: min(end - begin, 256), at least 0
+__device__ __forceinline__ int tile_extent(int64_t end, int64_t begin) {
+  const int64_t n = end - begin;
+  return n <= 0 ? 0 : n >= 256 ? 256 : (int)n;
+}
 
 // Row-split kernels: EPI_STORE (C), EPI_GELU_FWD (C = GELU'(Z) | C2 = GELU(Z))
 // and the SwiGLU gate|up pair (C = dH/dA | dH/dB at column f and c_split + f,
@@ -400,11 +444,15 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
   constexpr int HOFF = PAIR ? (SAVE ? 256 : 0) : (SAVE ? 256 : 0);  // column of the hidden activation
   const StagedTile<bf16, SC> st{(lds_char*)smem};
   bf16* C = reinterpret_cast<bf16*>(a.C);
-  bf16* C2 = reinterpret_cast<bf16*>(a.C2);
   const int wm = wave / 4;
   const int sr = 32 * wm + (lane & 31);  // this lane's staged row
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  const int rl = tile_extent(row_end, row_begin), nl = tile_extent(N, n0);
+  const uint32_t ldc = (uint32_t)a.ldc, ldc2 = (uint32_t)a.ldc2;
+  bf16* const Cp = C + row_begin * a.ldc + n0;
+  bf16* const Cup = PAIR ? Cp + a.c_split : Cp;
+  bf16* const C2p = (GELU || PAIR) ? reinterpret_cast<bf16*>(a.C2) + row_begin * a.ldc2 + n0 : Cp;
+  static_for<0, FM>([&](auto pass) {
+    constexpr int i = decltype(pass)::value;
     float scale = 1.0f;
     if constexpr (SCAT) {  // this lane's row's weight
       const int64_t rr = row_begin + wm * 128 + 32 * i + (lane & 31);
@@ -454,24 +502,31 @@ __device__ __forceinline__ void rows_epilogue_staged(const Args& a, f32x16 (&acc
       }
     }
     __syncthreads();
-    st.template store_all<512>([&](int r, int col, const u32x4& v) {
-      const int64_t rr = row_begin + (r >> 5) * 128 + 32 * i + (r & 31);
-      if (rr >= row_end) return;
-      if constexpr (PAIR) {
-        const int part = SAVE ? col >> 7 : 2, c = col & 127;  // 0: A, 1: B, 2: H
-        if (n0 + c >= N) return;
-        if (part == 0) st16(C + rr * a.ldc + n0 + c, v);
-        else if (part == 1) st16(C + rr * a.ldc + a.c_split + n0 + c, v);
-        else st16(C2 + rr * a.ldc2 + n0 + c, v);
-      } else {
-        const int c = col & 255;
-        if (n0 + c >= N) return;
-        if (GELU && (!SAVE || col >= 256)) st16(C2 + rr * a.ldc2 + n0 + c, v);
-        else if (SCAT) st16(C + (int64_t)a.scatter[rr] * a.ldc + n0 + c, v);
-        else st16(C + rr * a.ldc + n0 + c, v);
-      }
-    });
-  }
+    // staged row r is tile row (r / 32) 128 + 32 i + r % 32
+    auto to = [&](bf16* const base, const uint32_t ld) {
+      return [&, base, ld](int r, int c, const u32x4& v) {
+        const int tr = (r >> 5) * 128 + 32 * i + (r & 31);
+        if (tr < rl && c < nl) st16(base + tile_off(tr, ld, c), v);
+      };
+    };
+    if constexpr (PAIR && SAVE) {  // dH/dA | dH/dB | H
+      st.template store_part<512, 3, 0>(to(Cp, ldc));
+      st.template store_part<512, 3, 1>(to(Cup, ldc));
+      st.template store_part<512, 3, 2>(to(C2p, ldc2));
+    } else if constexpr (GELU && SAVE) {  // GELU'(Z) | GELU(Z)
+      st.template store_part<512, 2, 0>(to(Cp, ldc));
+      st.template store_part<512, 2, 1>(to(C2p, ldc2));
+    } else if constexpr (PAIR || GELU) {  // H only
+      st.template store_part<512, 1, 0>(to(C2p, ldc2));
+    } else if constexpr (SCAT) {
+      st.template store_part<512, 1, 0>([&](int r, int c, const u32x4& v) {
+        const int tr = (r >> 5) * 128 + 32 * i + (r & 31);
+        if (tr < rl && c < nl) st16(C + (int64_t)a.scatter[row_begin + tr] * a.ldc + n0 + c, v);
+      });
+    } else {
+      st.template store_part<512, 1, 0>(to(Cp, ldc));
+    }
+  });
 }
 
 // Activation backward of the row-split DGRAD kernels, staged the same way:
@@ -489,8 +544,11 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
   constexpr bool SW = EPI == gemm::EPI_SWIGLU_BWD;
   constexpr int PER = 64 * 32 / 512;  // 8-column groups per thread per pass
   const StagedTile<float, 256> st{(lds_char*)smem};
-  bf16* C = reinterpret_cast<bf16*>(a.C);
-  const bf16* X1 = reinterpret_cast<const bf16*>(a.X1);
+  const int rl = tile_extent(row_end, row_begin), nl = tile_extent(N, n0);
+  const uint32_t ldc = (uint32_t)a.ldc, ldx = (uint32_t)a.ldx;
+  bf16* const Cp = reinterpret_cast<bf16*>(a.C) + row_begin * a.ldc + n0;
+  bf16* const Cup = Cp + a.c_split;
+  const bf16* const Xp = reinterpret_cast<const bf16*>(a.X1) + row_begin * a.ldx + n0;
   const int sr = 32 * (wave / 4) + (lane & 31);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -506,17 +564,17 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
       }
     __syncthreads();
     // group u of this thread: staged row r = q / 32, columns 8 (q % 32) .. +7
-    int64_t rr[PER], nn[PER];
+    uint32_t co[PER];  // element offset of the group in the tile, for C (X1 has its own)
     bool ok[PER];
     u32x4 x0[PER], x1[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = (int)threadIdx.x + 512 * u, r = q >> 5, c8 = (q & 31) * 8;
-      rr[u] = row_begin + (r >> 5) * 128 + 32 * i + (r & 31);
-      nn[u] = n0 + c8;
-      ok[u] = rr[u] < row_end && nn[u] < N;
+      const int tr = (r >> 5) * 128 + 32 * i + (r & 31);  // row of the tile
+      ok[u] = tr < rl && c8 < nl;
+      co[u] = tile_off(tr, ldc, c8);
       // unconditional loads from a valid place (the tile's first row and column) when out of range
-      const bf16* xp = X1 + (ok[u] ? rr[u] * a.ldx + nn[u] : row_begin * a.ldx + n0);
+      const bf16* xp = Xp + (ok[u] ? tile_off(tr, ldx, c8) : 0u);
       x0[u] = ld16(xp);
       if constexpr (SW) x1[u] = ld16(xp + a.c_split);
     }
@@ -542,14 +600,14 @@ __device__ __forceinline__ void rows_epilogue_staged_bwd(const Args& a, f32x16 (
           db[e] = g8[e] * d1[e];
         }
         if (ok[u]) {
-          st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(da));
-          st16(C + rr[u] * a.ldc + a.c_split + nn[u], pack16<bf16>(db));
+          st16(Cp + co[u], pack16<bf16>(da));
+          st16(Cup + co[u], pack16<bf16>(db));
         }
       } else {
         float dz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) dz[e] = g8[e] * d0[e];
-        if (ok[u]) st16(C + rr[u] * a.ldc + nn[u], pack16<bf16>(dz));
+        if (ok[u]) st16(Cp + co[u], pack16<bf16>(dz));
       }
     }
   }
@@ -563,8 +621,15 @@ __device__ __forceinline__ void wgrad_epilogue_staged(const Args& a, f32x16 (&ac
                                                       int64_t N, char* smem) {
   static_assert(FM == 4 && FN == 2, "256 x 256 tile of 8 waves in 2 x 4");
   const StagedTile<T, 256> st{(lds_char*)smem};
-  T* C = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride;
-  T* C2 = a.C2 ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride : nullptr;
+  constexpr bool SPLIT = EPI == gemm::EPI_STORE_SPLITN;
+  const int ml = tile_extent(M, m0), nl = tile_extent(N, n0);
+  const uint32_t ldc = (uint32_t)a.ldc;
+  T* const Cp = reinterpret_cast<T*>(a.C) + (int64_t)wi * a.c_gstride + m0 * a.ldc + n0;
+  // columns n >= c_split go to C2 at column n - c_split: tile columns from cs on
+  const int cs = SPLIT ? tile_extent(a.c_split, n0) : 256;
+  T* const C2p = SPLIT ? reinterpret_cast<T*>(a.C2) + (int64_t)wi * a.c_gstride + m0 * a.ldc +
+                             (n0 > a.c_split ? n0 - a.c_split : 0)
+                       : Cp;
   const int wm = wave / 4;
   const int sr = 32 * wm + (lane & 31);
 #pragma unroll
@@ -581,14 +646,13 @@ __device__ __forceinline__ void wgrad_epilogue_staged(const Args& a, f32x16 (&ac
       }
     __syncthreads();
     st.template store_all<512>([&](int r, int col, const u32x4& v) {
-      const int64_t m = m0 + (r >> 5) * 128 + 32 * i + (r & 31);
-      const int64_t n = n0 + col;
-      if (m >= M || n >= N) return;
+      const int tr = (r >> 5) * 128 + 32 * i + (r & 31);  // row of the tile
+      if (tr >= ml || col >= nl) return;
       // c_split is a multiple of 8: a chunk never straddles it
-      if (EPI == gemm::EPI_STORE_SPLITN && n >= a.c_split)
-        st16(C2 + m * a.ldc + (n - a.c_split), v);
+      if (SPLIT && col >= cs)
+        st16(C2p + tile_off(tr, ldc, col - cs), v);
       else
-        st16(C + m * a.ldc + n, v);
+        st16(Cp + tile_off(tr, ldc, col), v);
     });
   }
 }
