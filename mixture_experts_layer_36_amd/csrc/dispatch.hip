@@ -15,8 +15,9 @@
 //   2. rows: per block, the sums of the block counts before it and in all
 //      (each workgroup reduces them itself, so no separate scan launch) give
 //      the per-expert bases, raw / kept counts, slot offsets and send
-//      segments; each token's rank among the block's earlier tokens (64-bit
-//      wave ballots + popcount, then a prefix over the 4 waves) gives pos, the
+//      segments; each token's rank among the block's earlier tokens (a 64-bit
+//      wave ballot per expert and the count of set bits below the lane, then
+//      a prefix over the 4 waves) gives pos, the
 //      kept flag, the row, row_of and assign_of_row;
 //   3. copy: each kept token row is read once and written to its <= k rows
 //      (16-byte loads / stores, coalesced along the row).
@@ -143,6 +144,7 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
   __shared__ int base_s[64];
   __shared__ int64_t start_s[64];
   __shared__ int wave_cnt[NW][64];
+  __shared__ uint8_t rank_s[NW][64][64];  // [wave][expert][lane]: rank among the wave's earlier lanes
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
   const int64_t t = (int64_t)b * NT + tid;
@@ -166,22 +168,26 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_rows_kernel(
     tot_s[tid] = tot;
   }
 
-  // c (first half). ranks within the wave, and the wave's count per expert
-  int rank[8];
+  // c (first half). ranks within the wave, and the wave's count per expert.
+  // Bit e of the lane's mask is set when one of its choices is expert e (a
+  // token picks an expert at most once); per expert, a ballot of that bit
+  // and the count of set bits below the lane (mbcnt) give the rank, which
+  // the lane leaves in LDS and reads back for its k choices afterwards.
+  uint32_t em[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) rank[j] = 0;
-  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int j = 0; j < 8; ++j)
+    if (my_e[j] >= 0 && my_e[j] < E) em[my_e[j] >> 5] |= 1u << (my_e[j] & 31);
   for (int e = 0; e < E; ++e) {
-    bool c = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) c |= (my_e[j] == e);
+    const bool c = (em[e >> 5] >> (e & 31)) & 1u;
     const unsigned long long mask = __ballot(c);
-    const int before = __popcll(mask & lt);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (my_e[j] == e) rank[j] = before;
+    const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (c) rank_s[w][e][lane] = (uint8_t)before;
     if (lane == 0) wave_cnt[w][e] = __popcll(mask);
   }
+  int rank[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rank[j] = (my_e[j] >= 0 && my_e[j] < E) ? rank_s[w][my_e[j]][lane] : 0;
   __syncthreads();
 
   // a (end) and b. wave 0: lane e holds expert e's base and raw count; lane s
