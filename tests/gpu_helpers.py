@@ -150,6 +150,25 @@ def run_full_parity(wl, inp, dot_floor=False, pipeline_chunks=0):
     errs["y"] = assert_close("y", host(layer.y), ref["y"], tol)
     if n > 0:
         errs["y_perm"] = assert_close("y_perm", host(layer.y_perm[:n]), ref["o_perm"], tol)
+        # the expert rows' hidden activation and the saved factors of its
+        # derivative (GELU'(Z), or dh/dA | dh/dB), in the send-buffer layout
+        F, off, order = wl.ffn, ref["layout"]["expert_offsets"], ref["layout"]["slot_expert"]
+        swiglu = wl.act == "swiglu"
+        h_ref = np.zeros((n, F))
+        a_ref = np.zeros((n, 2 * F if swiglu else F))
+        for s in range(wl.E):
+            r0, r1 = int(off[s]), int(off[s + 1])
+            if r1 == r0:
+                continue
+            f = ref["per_expert"][int(order[s])]
+            h_ref[r0:r1] = f["h"]
+            fac = oracle.activation_factors(f, wl.act)
+            if swiglu:
+                a_ref[r0:r1, :F], a_ref[r0:r1, F:] = fac["d1"], fac["d2"]
+            else:
+                a_ref[r0:r1] = fac["d"]
+        errs["h"] = assert_close("h", host(layer.h[:n]), h_ref, tol)
+        errs["act_saved"] = assert_close("act_saved", host(layer.act_saved[:n]), a_ref, tol)
     if dot_floor:
         terms = dot_abs_terms(oracle.to_f64(inp.dy), ref["o_perm"], ref["layout"]["row_of"].reshape(wl.T, wl.k))
         errs["d_topk_w"] = assert_dot_close("d_topk_w", host(layer.d_topk_w), ref["d_topk_w"], terms, wl.d, tol)

@@ -6,7 +6,9 @@ Routing indices, counts, offsets, send layout, row maps and the permuted rows
 are compared bit for bit, with the oracle routing on the GPU's own fp32
 logits.  Every workload is compared element by element: the three smaller
 ones here, the Mixtral- and DeepSeek-V2-Lite-shaped ones expert by expert in
-test_gpu_large.py.
+test_gpu_large.py.  The expert rows' hidden activation h and the saved
+factors of its derivative (act_saved: GELU'(Z), or dh/dA | dh/dB) are
+compared too, against oracle.activation_factors of the oracle's own forward.
 """
 import os
 import sys
