@@ -80,6 +80,11 @@ CASES = {
     "T300_d8192_E8": (300, 8192, 8, 2, "softmax_topk", None, 112),
     # more than 16 experts: the per-block kernel
     "T500_d1024_E32": (500, 1024, 32, 4, "softmax_topk_renorm", 1.0, 113),
+    # more than 32 experts: the per-block kernel with 32 tokens per workgroup
+    # (the DeepSeek-V2-Lite router shape, 16384 / 32 workgroups, k = 6)
+    "T16384_d2048_E64_k6": (16384, 2048, 64, 6, "softmax_topk", None, 118),
+    # ... a partial last workgroup, 40 experts, d ending inside a 32-K block
+    "T1001_d520_E40_k3": (1001, 520, 40, 3, "topk_softmax", 1.0, 119),
 }
 
 
