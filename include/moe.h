@@ -286,7 +286,12 @@ int moe_expert_ffn_bwd_weights(const moe_config* cfg, const moe_groups* grp,
  *   dw_in, dw_up, dw_out: same shapes and dtype as w_in, w_up, w_out;
  *   weight sets with no rows get exact zeros.
  *   ws: moe_plan's workspace (holds dL/dZ or dL/d[A|B] in dtype, then the
- *       fp32 partials of weight gradients split over their rows).
+ *       fp32 partials of weight gradients split over their rows; in bf16
+ *       with at least 2000 (1 + m) / m rows per weight set on average, m = 2
+ *       for SwiGLU else 1, then also a transposed copy of the three weight
+ *       tensors, made in this call, that both dgrads read; moe_plan sizes
+ *       the workspace for it and the call does without it when a table's
+ *       copy would not fit).
  * Errors: MOE_ERR_INVALID also when the group table would need more
  *   workspace than moe_plan's workspace_bytes for cfg (a table with more
  *   groups, rows or hidden width than the routed or shared tables above), or

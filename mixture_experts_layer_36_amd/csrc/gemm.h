@@ -68,5 +68,10 @@ bool supports(const gemm::Args& a);
 int wgrad_ksplit(int64_t groups, int64_t M, int64_t N, int64_t rows_max);
 hipError_t run_rows_bf16(int kind, int epi, const gemm::Args& a, int64_t rows_max, hipStream_t st);
 hipError_t run_wgrad_bf16(int epi, const gemm::Args& a, hipStream_t st);
+// bf16 batched transpose: dst[b * dst_bstride + c * rows + r] =
+// src[b * src_bstride + r * cols + c] for b < batches, r < rows, c < cols;
+// rows and cols multiples of 8, both pointers 16-byte aligned.
+hipError_t transpose_bf16(const void* src, void* dst, int64_t batches, int64_t rows, int64_t cols,
+                          int64_t src_bstride, int64_t dst_bstride, hipStream_t st);
 }  // namespace gemm3
 }  // namespace moe

@@ -1030,6 +1030,9 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
       case EPI_STORE_SCATTER: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_STORE_SCATTER>(a, rows_max, st);
       case EPI_GELU_FWD_H: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_GELU_FWD_H>(a, rows_max, st);
       case EPI_SWIGLU_FWD_H: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_SWIGLU_FWD_H>(a, rows_max, st);
+      // dgrads over transposed weights (N-contiguous, the forward's loads)
+      case EPI_GELU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_GELU_BWD>(a, rows_max, st);
+      case EPI_SWIGLU_BWD: return launch_rows<MOE_GEMM3_CFG_PP, KIND_FWD, EPI_SWIGLU_BWD>(a, rows_max, st);
     }
   } else {
     switch (epi) {
@@ -1039,6 +1042,57 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
     }
   }
   return hipErrorInvalidValue;
+}
+
+// Weights transposed for the backward (forward-kind dgrads): a workgroup
+// moves a 64 x 64 tile through LDS, reading 64 rows x 128 bytes and writing
+// 64 rows x 128 bytes of the transpose, 16 bytes per thread access.  The LDS
+// rows are padded to 144 bytes, so the column reads of the write phase spread
+// over the banks.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int64_t rows, int64_t cols,
+                                                             int64_t sbs, int64_t dbs) {
+  constexpr int P = 72;  // LDS row pitch in elements
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * P];
+  const int tid = (int)threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const uint16_t* s = src + (int64_t)blockIdx.z * sbs;
+  uint16_t* d = dst + (int64_t)blockIdx.z * dbs;
+  u32x4 v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // 8-element chunk q: tile row q / 8, columns 8 (q % 8) ..
+    const int q = tid + 256 * j, tr = q >> 3, tc = (q & 7) * 8;
+    const int64_t r = r0 + tr, c = c0 + tc;
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) v[j] = ld16(s + r * cols + c);  // rows and cols are multiples of 8
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = tid + 256 * j, tr = q >> 3, tc = (q & 7) * 8;
+    *reinterpret_cast<u32x4*>(&t[tr * P + tc]) = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // output chunk q: tile column q / 8, tile rows 8 (q % 8) ..
+    const int q = tid + 256 * j, tc = q >> 3, tr = (q & 7) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)t[(tr + 2 * i) * P + tc] | ((uint32_t)t[(tr + 2 * i + 1) * P + tc] << 16);
+    const int64_t c = c0 + tc, r = r0 + tr;
+    if (c < cols && r < rows) st16(d + c * rows + r, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+hipError_t transpose_bf16(const void* src, void* dst, int64_t batches, int64_t rows, int64_t cols,
+                          int64_t src_bstride, int64_t dst_bstride, hipStream_t st) {
+  if (batches <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows % 8 || cols % 8 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return hipErrorInvalidValue;
+  const int64_t gx = (cols + 63) / 64, gy = (rows + 63) / 64;
+  if (gx > 0x7fffffff || gy > 65535 || batches > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)batches), dim3(256), 0, st,
+                     (const uint16_t*)src, (uint16_t*)dst, rows, cols, src_bstride, dst_bstride);
+  return hipGetLastError();
 }
 
 int wgrad_ksplit(int64_t groups, int64_t M, int64_t N, int64_t rows_max) {

@@ -88,6 +88,18 @@ FUZZ = {
     "T70_E20_f32": W("T70_E20_f32", T=70, d=56, ffn=32, E=20, k=1, capacity_factor=2.0,
                      gating="softmax_topk", act="gelu", dtype="f32", ep_ranks=4, placement="round_robin",
                      seed=26),
+    # bf16 backward on transposed weights (at least 2000 rows per weight set
+    # times m / (1 + m)): SwiGLU with round-robin placement and d, ffn that
+    # end inside a 64-wide transpose tile; GELU on one expert; and the shared
+    # experts' table alone (the routed one stays below the threshold)
+    "T6144_E4_rr_swiglu_wt": W("T6144_E4_rr_swiglu_wt", T=6144, d=136, ffn=264, E=4, k=2,
+                               capacity_factor=0.0, gating="softmax_topk", act="swiglu", dtype="bf16",
+                               ep_ranks=2, placement="round_robin", seed=27),
+    "T4200_E1_gelu_wt": W("T4200_E1_gelu_wt", T=4200, d=72, ffn=40, E=1, k=1, capacity_factor=0.0,
+                          gating="softmax_topk", act="gelu", dtype="bf16", seed=28),
+    "T3200_E4_shared_wt": W("T3200_E4_shared_wt", T=3200, d=64, ffn=32, E=4, k=2, capacity_factor=0.0,
+                            gating="topk_softmax", act="swiglu", dtype="bf16", n_shared=1, ffn_shared=48,
+                            seed=29),
     # weight-gradient launches with few tiles and long reductions split the
     # reduction into fp32 partials: the shared experts here (4 splits of
     # 1024 tokens) and the 2 routed experts of the next case (4 splits)
