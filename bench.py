@@ -250,7 +250,10 @@ def main():
     launches = 6 * (2 if wl.n_shared else 1)
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    roofline = {"kernel": f"grouped expert GEMM, fwd+bwd ({launches} launches per step)",
+    # timed as the expert FFN entry points: the split-reduction and weight-transpose
+    # kernels inside them count as GEMM time
+    roofline = {"kernel": f"grouped expert GEMM, fwd+bwd ({launches} launches per step, with their "
+                          "split reductions and weight transposes)",
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
                 "per_step_flops": gemm_flops, "per_step_ms": round(gemm_ms, 4)}
