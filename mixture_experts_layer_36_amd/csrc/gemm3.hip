@@ -1046,16 +1046,23 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
 
 // Weights transposed for the backward (forward-kind dgrads): a workgroup
 // moves a 64 x 64 tile through LDS, reading 64 rows x 128 bytes and writing
-// 64 rows x 128 bytes of the transpose, 16 bytes per thread access.  The LDS
-// rows are padded to 144 bytes, so the column reads of the write phase spread
-// over the banks.
+// 64 rows x 128 bytes of the transpose, 16 bytes per thread access.  In LDS
+// the tile's rows are unpadded and the 8 16-byte chunks of row r sit in the
+// order chunk ^ (r / 8): the 8 lanes of a row write its 128 bytes, and the
+// 64 lanes of a column read (8 columns of one chunk x 8 row groups) fall on
+// 8 different chunks, 32 different banks.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
                                                              uint16_t* __restrict__ dst, int64_t rows, int64_t cols,
                                                              int64_t sbs, int64_t dbs) {
-  constexpr int P = 72;  // LDS row pitch in elements
-  __shared__ __attribute__((aligned(16))) uint16_t t[64 * P];
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * 64];
   const int tid = (int)threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  // consecutive workgroups walk 8 row tiles per column tile, so that the
+  // ones in flight write 1 KB runs of each transposed row as well as read
+  // runs of each source row
+  const int gx = (int)((cols + 63) >> 6), gy = (int)((rows + 63) >> 6);
+  const int L = (int)blockIdx.x, grp = L / (8 * gx), rem = L - grp * 8 * gx;
+  const int gsz = gy - grp * 8 < 8 ? gy - grp * 8 : 8;
+  const int64_t r0 = (int64_t)(grp * 8 + rem % gsz) * 64, c0 = (int64_t)(rem / gsz) * 64;
   const uint16_t* s = src + (int64_t)blockIdx.z * sbs;
   uint16_t* d = dst + (int64_t)blockIdx.z * dbs;
   u32x4 v[2];
@@ -1068,18 +1075,18 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int q = tid + 256 * j, tr = q >> 3, tc = (q & 7) * 8;
-    *reinterpret_cast<u32x4*>(&t[tr * P + tc]) = v[j];
+    const int q = tid + 256 * j, tr = q >> 3, ch = q & 7;
+    *reinterpret_cast<u32x4*>(&t[tr * 64 + ((ch ^ (tr >> 3)) << 3)]) = v[j];
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 2; ++j) {  // output chunk q: tile column q / 8, tile rows 8 (q % 8) ..
-    const int q = tid + 256 * j, tc = q >> 3, tr = (q & 7) * 8;
+    const int q = tid + 256 * j, tc = q >> 3, g = q & 7;
+    const uint16_t* col = t + g * 8 * 64 + (((tc >> 3) ^ g) << 3) + (tc & 7);
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)t[(tr + 2 * i) * P + tc] | ((uint32_t)t[(tr + 2 * i + 1) * P + tc] << 16);
-    const int64_t c = c0 + tc, r = r0 + tr;
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)col[(2 * i) * 64] | ((uint32_t)col[(2 * i + 1) * 64] << 16);
+    const int64_t c = c0 + tc, r = r0 + 8 * g;
     if (c < cols && r < rows) st16(d + c * rows + r, u32x4{w[0], w[1], w[2], w[3]});
   }
 }
@@ -1089,8 +1096,8 @@ hipError_t transpose_bf16(const void* src, void* dst, int64_t batches, int64_t r
   if (batches <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
   if (rows % 8 || cols % 8 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return hipErrorInvalidValue;
   const int64_t gx = (cols + 63) / 64, gy = (rows + 63) / 64;
-  if (gx > 0x7fffffff || gy > 65535 || batches > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)batches), dim3(256), 0, st,
+  if (gx * gy > 0x7fffffff / 8 || batches > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(gx * gy), 1, (unsigned)batches), dim3(256), 0, st,
                      (const uint16_t*)src, (uint16_t*)dst, rows, cols, src_bstride, dst_bstride);
   return hipGetLastError();
 }
