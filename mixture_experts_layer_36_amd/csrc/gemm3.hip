@@ -1054,39 +1054,41 @@ hipError_t run_rows_bf16(int kind, int epi, const Args& a, int64_t rows_max, hip
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
                                                              uint16_t* __restrict__ dst, int64_t rows, int64_t cols,
                                                              int64_t sbs, int64_t dbs) {
+  using namespace gemm_addr;
   __shared__ __attribute__((aligned(16))) uint16_t t[64 * 64];
   const int tid = (int)threadIdx.x;
   // consecutive workgroups walk 8 row tiles per column tile, so that the
   // ones in flight write 1 KB runs of each transposed row as well as read
   // runs of each source row
-  const int gx = (int)((cols + 63) >> 6), gy = (int)((rows + 63) >> 6);
-  const int L = (int)blockIdx.x, grp = L / (8 * gx), rem = L - grp * 8 * gx;
-  const int gsz = gy - grp * 8 < 8 ? gy - grp * 8 : 8;
-  const int64_t r0 = (int64_t)(grp * 8 + rem % gsz) * 64, c0 = (int64_t)(rem / gsz) * 64;
+  int64_t r0, c0;
+  transpose_tile((int)blockIdx.x, rows, cols, r0, c0);
   const uint16_t* s = src + (int64_t)blockIdx.z * sbs;
   uint16_t* d = dst + (int64_t)blockIdx.z * dbs;
   u32x4 v[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {  // 8-element chunk q: tile row q / 8, columns 8 (q % 8) ..
-    const int q = tid + 256 * j, tr = q >> 3, tc = (q & 7) * 8;
+  for (int j = 0; j < 2; ++j) {  // 8-element chunk: tile row tr, columns tc ..
+    int tr, tc;
+    transpose_load_lane(tid, j, tr, tc);
     const int64_t r = r0 + tr, c = c0 + tc;
     v[j] = u32x4{0u, 0u, 0u, 0u};
     if (r < rows && c < cols) v[j] = ld16(s + r * cols + c);  // rows and cols are multiples of 8
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int q = tid + 256 * j, tr = q >> 3, ch = q & 7;
-    *reinterpret_cast<u32x4*>(&t[tr * 64 + ((ch ^ (tr >> 3)) << 3)]) = v[j];
+    int tr, tc;
+    transpose_load_lane(tid, j, tr, tc);
+    *reinterpret_cast<u32x4*>(&t[transpose_lds(tr, tc >> 3)]) = v[j];
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {  // output chunk q: tile column q / 8, tile rows 8 (q % 8) ..
-    const int q = tid + 256 * j, tc = q >> 3, g = q & 7;
-    const uint16_t* col = t + g * 8 * 64 + (((tc >> 3) ^ g) << 3) + (tc & 7);
+  for (int j = 0; j < 2; ++j) {  // output chunk: tile column tc, tile rows tr .. tr + 7
+    int tc, tr;
+    transpose_store_lane(tid, j, tc, tr);
+    const uint16_t* col = t + transpose_lds(tr, tc >> 3) + (tc & 7);  // rows tr .. tr + 7 share the chunk order
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)col[(2 * i) * 64] | ((uint32_t)col[(2 * i + 1) * 64] << 16);
-    const int64_t c = c0 + tc, r = r0 + 8 * g;
+    const int64_t c = c0 + tc, r = r0 + tr;
     if (c < cols && r < rows) st16(d + c * rows + r, u32x4{w[0], w[1], w[2], w[3]});
   }
 }

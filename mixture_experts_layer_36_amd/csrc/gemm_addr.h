@@ -250,5 +250,30 @@ MOE_HD StageWalk wgrad_walk(int64_t r0, int64_t c0, int BK, int64_t ld) {
   return stage_walk((r0 * ld + c0) * 2, BK, ld * 2, c0 * 2);
 }
 
+// Weight transpose (64 x 64 tiles, 256 threads): workgroup L's tile, with
+// consecutive workgroups walking 8 row tiles per column tile.
+MOE_HD void transpose_tile(int L, int64_t rows, int64_t cols, int64_t& r0, int64_t& c0) {
+  const int gx = (int)((cols + 63) >> 6), gy = (int)((rows + 63) >> 6);
+  const int grp = L / (8 * gx), rem = L - grp * 8 * gx;
+  const int gsz = gy - grp * 8 < 8 ? gy - grp * 8 : 8;
+  r0 = (int64_t)(grp * 8 + rem % gsz) * 64;
+  c0 = (int64_t)(rem / gsz) * 64;
+}
+// LDS element of tile row tr's 16-byte chunk ch (rows unpadded, the chunks of
+// row tr in the order ch ^ (tr / 8 % 8)).
+MOE_HD int transpose_lds(int tr, int ch) { return tr * 64 + ((ch ^ ((tr >> 3) & 7)) << 3); }
+// Thread tid's j-th source chunk (tile row, first column) and j-th output
+// chunk (tile column, first of 8 tile rows), j = 0, 1.
+MOE_HD void transpose_load_lane(int tid, int j, int& tr, int& tc) {
+  const int q = tid + 256 * j;
+  tr = q >> 3;
+  tc = (q & 7) * 8;
+}
+MOE_HD void transpose_store_lane(int tid, int j, int& tc, int& tr) {
+  const int q = tid + 256 * j;
+  tc = q >> 3;
+  tr = (q & 7) * 8;
+}
+
 }  // namespace gemm_addr
 }  // namespace moe

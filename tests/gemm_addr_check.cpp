@@ -26,6 +26,7 @@
 // violation, exit status 1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <set>
@@ -278,6 +279,57 @@ void check_wgrad(const WgradLaunch& L, const std::vector<int64_t>& off, int grou
   }
 }
 
+// The weight transpose over a [rows][cols] source: every workgroup's tile
+// inside the grid and each tile once, every source load and output store in
+// bounds, each LDS chunk written once per tile, each output chunk's 8 column
+// elements read from the LDS slots its source rows were written to, and every
+// output element written exactly once with the source element it transposes.
+void check_transpose(const char* name, int64_t rows, int64_t cols) {
+  const int64_t gx = (cols + 63) / 64, gy = (rows + 63) / 64;
+  std::vector<uint8_t> done((size_t)(rows * cols), 0);
+  std::vector<int64_t> lds(64 * 64);
+  std::set<std::pair<int64_t, int64_t>> tiles;
+  for (int L = 0; L < (int)(gx * gy); ++L) {
+    int64_t r0, c0;
+    transpose_tile(L, rows, cols, r0, c0);
+    if (r0 < 0 || c0 < 0 || r0 >= gy * 64 || c0 >= gx * 64 || r0 % 64 || c0 % 64 || !tiles.insert({r0, c0}).second)
+      fail(std::string(name) + ": transpose tile outside the grid or repeated");
+    std::fill(lds.begin(), lds.end(), -1);
+    for (int tid = 0; tid < 256; ++tid)
+      for (int j = 0; j < 2; ++j) {
+        int tr, tc;
+        transpose_load_lane(tid, j, tr, tc);
+        const int a = transpose_lds(tr, tc >> 3);
+        if (tr < 0 || tr >= 64 || tc < 0 || tc > 56 || tc % 8 || a < 0 || a + 8 > 64 * 64 || a % 8)
+          fail(std::string(name) + ": transpose LDS write outside the tile");
+        for (int e = 0; e < 8; ++e) {
+          if (lds[a + e] != -1) fail(std::string(name) + ": transpose LDS slot written twice");
+          const int64_t r = r0 + tr, c = c0 + tc + e;
+          lds[a + e] = r < rows && c < cols ? r * cols + c : -2;  // -2: zero filler
+        }
+      }
+    for (int tid = 0; tid < 256; ++tid)
+      for (int j = 0; j < 2; ++j) {
+        int tc, tr;
+        transpose_store_lane(tid, j, tc, tr);
+        const int64_t c = c0 + tc, r = r0 + tr;
+        if (!(c < cols && r < rows)) continue;
+        const int base = transpose_lds(tr, tc >> 3) + (tc & 7);
+        for (int e = 0; e < 8; ++e) {
+          const int a = base + e * 64;
+          if (a < 0 || a >= 64 * 64) fail(std::string(name) + ": transpose LDS read outside the tile");
+          const int64_t src = lds[a], o = c * rows + r + e;
+          if (o < 0 || o >= rows * cols) fail(std::string(name) + ": transpose store outside the output");
+          if (src != (r + e) * cols + c) fail(std::string(name) + ": transpose output element from the wrong source");
+          if (done[o]++) fail(std::string(name) + ": transpose output element written twice");
+          ++g_checked;
+        }
+      }
+  }
+  for (uint8_t v : done)
+    if (v != 1) fail(std::string(name) + ": transpose output element never written");
+}
+
 }  // namespace
 
 int main() {
@@ -331,6 +383,18 @@ int main() {
     if (b_split % BK == 0)  // otherwise the register-staged kernels take this launch
       check_rows({"dgrad W_in", true, false, dact, w_in, swiglu ? w_up : w_in, m * F, F, d * F, d, m * F, b_split},
                  o, ends, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
+  }
+  // backward on transposed weights (bf16 calls with many rows per weight
+  // set): both dgrads as forward-kind launches over W_out^T [W][d][F] and
+  // [W_in^T | W_up^T] [W][m F][d], whole groups only
+  {
+    check_transpose("W_out [F][d]", F, d);
+    check_transpose("W_in [d][F]", d, F);
+    const Tensor wt_out{"W_out^T", W * d * F * 2}, wt_io{"[W_in | W_up]^T", W * m * F * d * 2};
+    check_rows({"dgrad W_out^T", false, false, dy, wt_out, wt_out, d, F, d * F, F, d, 0}, off, nullptr, (int)groups,
+               rows_max, (int)rr_R, (int)rr_L, W);
+    check_rows({"dgrad [W_in | W_up]^T", false, false, dact, wt_io, wt_io, m * F, d, m * F * d, d, m * F, 0}, off,
+               nullptr, (int)groups, rows_max, (int)rr_R, (int)rr_L, W);
   }
   // the fused forward's GEMM-1: rows gathered from T = rows_max tokens of x
   // through a synthetic assignment map (t*k + j, k = 2), every row a

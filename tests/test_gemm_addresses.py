@@ -2,7 +2,7 @@
 
 tests/gemm_addr_check.cpp enumerates, for one expert FFN call, every
 workgroup, wave, lane and load of the six bf16 GEMM launches of its forward
-and backward pass, through the same address functions the kernels use
+and backward pass (and of the two dgrads run on transposed weights), through the same address functions the kernels use
 (csrc/gemm_addr.h), and checks each load against the tensor it reads:
 aligned resources below the extent cap, every served load inside its tensor
 and at the element the tile needs, every needed element served and
