@@ -61,6 +61,24 @@ def test_plan_matches_capacity_definition(lib, name):
     assert s.workspace_bytes > 0 and s.workspace_bytes % 256 == 0
 
 
+def test_plan_reserves_transposed_weights_where_the_header_says(lib):
+    """In bf16, moe_plan's workspace holds a transposed copy of the three
+    expert weight tensors when the rows per weight set reach
+    2000 (1 + m) / m on average (m = 2 for SwiGLU, else 1), on top of
+    dL/d act; below that it does not."""
+    for name, T, d, F, E, k, act, want in [
+            ("Mixtral", 16384, 4096, 14336, 8, 2, "swiglu", True),     # 4096 rows per expert >= 3000
+            ("GPT-2", 8192, 768, 3072, 8, 2, "gelu", False),          # 2048 < 4000
+            ("GELU at 4000", 16000, 1024, 4096, 8, 2, "gelu", True),  # exactly 4000
+            ("GELU below", 15992, 1024, 4096, 8, 2, "gelu", False)]:  # 3998
+        m = 2 if act == "swiglu" else 1
+        s = nat.plan(nat.make_config(T, d, F, E, k, 0.0, "softmax_topk", act, "bf16"))
+        d_act = s.n_max * m * F * 2
+        wt = (1 + m) * E * d * F * 2
+        assert (s.workspace_bytes >= d_act + wt) == want, name
+        assert s.workspace_bytes >= d_act, name
+
+
 def test_plan_capacity_edge_values(lib):
     for T, E, k, cf in [(10, 3, 1, 1.0), (7, 64, 1, 0.01), (100, 2, 2, 5.0), (1000, 7, 3, 1.1),
                         (12345, 64, 6, 0.3), (1, 1, 1, 1.0)]:
