@@ -112,7 +112,7 @@ FUZZ = {
     # 8192, 0, 0) while the weight gradients split their reductions in 4: the
     # real items come first and the empty experts' zero partials after them
     # (with 4096 rows per expert on average, its dgrads run on transposed
-    # weights, two of which no row reads; so do the next case's)
+    # weights, two of which no row reads; so do those of T8192_E2_splitk)
     "T8192_E4_skew_splitk": W("T8192_E4_skew_splitk", T=8192, d=64, ffn=48, E=4, k=2, capacity_factor=0.0,
                               gating="softmax_topk", act="swiglu", dtype="bf16", zipf_s=1.2, seed=43),
     # a skewed routing (the longest expert holds more than twice the mean
