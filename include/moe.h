@@ -267,8 +267,9 @@ int moe_combine_fused(const moe_config* cfg, const void* y_tok,
  * the group table's rows (sub-ranges allowed: grp->ends), and
  * moe_expert_ffn_bwd_weights the weight gradients over whole groups (ends
  * NULL) from the dL/d act that data calls covering every row left in ws.
- * Nothing else may use ws in between.  Arguments, results and errors as in
- * moe_expert_ffn_bwd. */
+ * Nothing else may use ws in between.  These two read the weights as given
+ * (no transposed copy in ws), whatever the rows per weight set.  Arguments,
+ * results and errors as in moe_expert_ffn_bwd. */
 int moe_expert_ffn_bwd_data(const moe_config* cfg, const moe_groups* grp,
                             const void* w_in, const void* w_up,
                             const void* w_out, const void* act_saved,
